@@ -1,0 +1,171 @@
+"""Thin torch-facing binding of the C ABI: argument marshalling only.
+
+Every function hands device pointers of caller-owned torch tensors to libdllm.so and enqueues work
+on the current torch stream (or the stream given).  No part of the step, pack or compact
+computation runs here.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import DllmError, Meta, Queue, Reqs  # noqa: F401  (re-exported)
+
+_DT = {torch.bfloat16: _lib.DLLM_BF16, torch.float32: _lib.DLLM_FP32}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name, numel=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+
+
+def dllm_step_workspace_bytes(rows: int, L: int, V: int, dtype=torch.bfloat16) -> int:
+    return int(_lib.lib().dllm_step_workspace_bytes(rows, L, V, _DT[dtype]))
+
+
+def new_workspace(rows: int, L: int, V: int, dtype=torch.bfloat16, device="cuda"):
+    """A zero-filled step workspace (zeroed once; every call leaves it zeroed)."""
+    n = dllm_step_workspace_bytes(rows, L, V, dtype)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def dllm_step(logits, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status,
+              p=None, b=None, conf=None, argmax=None, rows=None, L=None, V=None, pos_stride=None,
+              row_stride=None, stream=None):
+    """One LowConfidence denoise step (see include/dllm.h).
+
+    logits: [rows, L, V] bf16/fp32 device tensor, or any tensor whose storage holds element
+    (r, j, v) at r*row_stride + j*pos_stride + v when the strides are given.
+    """
+    if logits.dtype not in _DT:
+        raise ValueError(f"logits dtype {logits.dtype} not supported")
+    if rows is None:
+        rows, L, V = logits.shape
+    if pos_stride is None:
+        pos_stride = logits.stride(1) if logits.dim() == 3 else V
+    if row_stride is None:
+        row_stride = logits.stride(0) if logits.dim() == 3 else L * pos_stride
+    W = input_ids.shape[-1]
+    _need(input_ids, torch.int32, "input_ids", rows * W)
+    _need(mask_in, torch.uint8, "mask_in", rows * L)
+    _need(mask_out, torch.uint8, "mask_out", rows * L)
+    _need(threshold, torch.float32, "threshold", rows)
+    _need(done, torch.uint8, "done", rows)
+    _need(accept_len, torch.int32, "accept_len", rows)
+    _need(workspace, torch.uint8, "workspace")
+    _need(status, torch.int32, "status", 1)
+    for t, dt, nm, n in ((p, torch.int32, "p", rows), (b, torch.int32, "b", rows),
+                         (conf, torch.float32, "conf", rows * L), (argmax, torch.int32, "argmax", rows * L)):
+        if t is not None:
+            _need(t, dt, nm, n)
+    rc = _lib.lib().dllm_step(_stream(stream), _ptr(logits), _DT[logits.dtype], pos_stride, row_stride, rows, L, V,
+                              _ptr(input_ids), W, _ptr(mask_in), _ptr(mask_out), _ptr(threshold), _ptr(p), _ptr(b),
+                              _ptr(conf), _ptr(argmax), _ptr(done), _ptr(accept_len), _ptr(workspace),
+                              workspace.numel(), _ptr(status))
+    _lib.check(rc, "dllm_step")
+
+
+class ReqTable:
+    """Device-resident request table (the fields of dllm_reqs), built from host numpy arrays."""
+
+    def __init__(self, p, K, b, state, threshold, arena_off, arena, blk_mask, device="cuda"):
+        def dev(a, dt):
+            return torch.as_tensor(a).to(dtype=dt).contiguous().to(device)
+        self.p = dev(p, torch.int32)
+        self.K = dev(K, torch.int32)
+        self.b = dev(b, torch.int32)
+        self.state = dev(state, torch.int32)
+        self.threshold = dev(threshold, torch.float32)
+        self.arena_off = dev(arena_off, torch.int64)
+        self.arena = dev(arena, torch.int32)
+        self.blk_mask = dev(blk_mask, torch.uint8)
+        self.L = int(self.blk_mask.shape[1])
+        self.n_req = int(self.p.shape[0])
+
+    def struct(self) -> Reqs:
+        return Reqs(self.n_req, self.p.data_ptr(), self.K.data_ptr(), self.b.data_ptr(), self.state.data_ptr(),
+                    self.threshold.data_ptr(), self.arena_off.data_ptr(), self.arena.data_ptr(),
+                    self.blk_mask.data_ptr())
+
+
+class DevQueue:
+    """Device-resident pending queue (dllm_queue): ids [cap] and a device length."""
+
+    def __init__(self, ids, device="cuda", cap=None):
+        ids = torch.as_tensor(ids).to(torch.int32)
+        cap = int(ids.numel()) if cap is None else int(cap)
+        self.ids = torch.full((max(cap, 1),), -1, dtype=torch.int32, device=device)
+        self.ids[:ids.numel()] = ids.to(device)
+        self.len = torch.tensor([ids.numel()], dtype=torch.int32, device=device)
+        self.cap = cap
+
+    def struct(self) -> Queue:
+        return Queue(self.ids.data_ptr(), self.len.data_ptr(), self.cap)
+
+
+def dllm_pack(rows, L, W, pad_id, row_req, reqs: ReqTable, box_ids, mask, threshold, p, b, status,
+              box_valid=None, box_pos=None, stream=None):
+    """Gather the left-padded box for rows [0, rows) (see include/dllm.h)."""
+    if rows > 0:
+        _need(row_req, torch.int32, "row_req", rows)
+        _need(box_ids, torch.int32, "box_ids", rows * W)
+        _need(mask, torch.uint8, "mask", rows * L)
+        _need(threshold, torch.float32, "threshold", rows)
+        _need(p, torch.int32, "p", rows)
+        _need(b, torch.int32, "b", rows)
+        _need(status, torch.int32, "status", 1)
+        if box_valid is not None:
+            _need(box_valid, torch.uint8, "box_valid", rows * W)
+        if box_pos is not None:
+            _need(box_pos, torch.int32, "box_pos", rows * W)
+    st = reqs.struct()
+    rc = _lib.lib().dllm_pack(_stream(stream), rows, L, W, pad_id, _ptr(row_req), ctypes.byref(st), _ptr(box_ids),
+                              _ptr(box_valid), _ptr(box_pos), _ptr(mask), _ptr(threshold), _ptr(p), _ptr(b),
+                              _ptr(status))
+    _lib.check(rc, "dllm_pack")
+
+
+def dllm_compact(rows, L, W, mask_id, eos_id, row_req, rows_cap, reqs: ReqTable, queue: DevQueue, budget, meta,
+                 status, box_ids=None, mask=None, done=None, stream=None):
+    """Commit finished blocks, evict, refill under the token budget (see include/dllm.h).
+    meta: device uint8 tensor of 32 bytes (a dllm_meta)."""
+    _need(row_req, torch.int32, "row_req", rows_cap)
+    _need(meta, torch.uint8, "meta", 32)
+    _need(status, torch.int32, "status", 1)
+    if box_ids is not None:
+        _need(box_ids, torch.int32, "box_ids", rows * W)
+        _need(mask, torch.uint8, "mask", rows * L)
+        _need(done, torch.uint8, "done", rows)
+    st = reqs.struct()
+    q = queue.struct()
+    rc = _lib.lib().dllm_compact(_stream(stream), rows, L, W, mask_id, eos_id, _ptr(box_ids), _ptr(mask), _ptr(done),
+                                 _ptr(row_req), rows_cap, ctypes.byref(st), ctypes.byref(q), int(budget), _ptr(meta),
+                                 _ptr(status))
+    _lib.check(rc, "dllm_compact")
+
+
+def read_meta(meta_tensor) -> dict:
+    """Copy a device dllm_meta to the host (synchronises with the tensor's stream)."""
+    raw = meta_tensor.cpu().numpy().tobytes()
+    m = Meta.from_buffer_copy(raw)
+    return dict(rows=m.rows, W=m.W, n_evicted=m.n_evicted, n_admitted=m.n_admitted, n_queued=m.n_queued,
+                cost=m.cost)

@@ -1,0 +1,165 @@
+"""Host loop driver: synchronous and first-done-first-out (FDFO) execution over libdllm.
+
+[FDFO] = page "FDFO: 让 dLLM 推理从「整批等最慢」变成「谁先完成谁先走」":
+  §工程设计一 — _run_sync() repeats forward -> step until every block of the batch is done;
+  _run_fdfo() runs forward -> step and hands the per-request done flags back to the scheduler.
+  §工程设计二 — the per-request accept lengths cross to the host (accept_length_per_req_cpu).
+  §工程设计四 — in-place re-loop: while no block of the batch finishes, keep denoising the same
+  batch; as soon as any finishes, yield to the scheduler.
+[BlockServe] = page "BlockServe: 块粒度连续批处理实现高吞吐扩散大语言模型服务", §II-C Algorithm 1:
+  admission, a block cycle, advance, evict, repeat until queue and active set are empty.
+
+The driver owns the device buffers and the loop rule only; pack, step and compact run in
+libdllm.so.  The model forward is not part of this library: the caller passes `forward`, which
+fills the session's logits buffer for the current box (a synthetic generator in tests/bench).
+Per step the only device-to-host traffic is the done flags and the new mask of the box rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import api
+
+
+class Session:
+    """Device state for one run: request table, queue, row map, box buffers and step workspace."""
+
+    def __init__(self, p, K, b, state, threshold, arena_off, arena, blk_mask, row_req, rows, queue, *, L, V,
+                 dtype=torch.bfloat16, rows_cap, budget=0, mask_id, pad_id, eos_id=-1, device="cuda",
+                 logits=None):
+        self.L, self.V, self.dtype = int(L), int(V), dtype
+        self.rows_cap, self.budget = int(rows_cap), int(budget)
+        self.mask_id, self.pad_id, self.eos_id = int(mask_id), int(pad_id), int(eos_id)
+        self.device = device
+        self.reqs = api.ReqTable(p, K, b, state, threshold, arena_off, arena, blk_mask, device=device)
+        self.queue = api.DevQueue(queue, device=device, cap=max(len(queue), 1))
+        rr = np.full(self.rows_cap, -1, np.int32)
+        rr[:rows] = np.asarray(row_req)[:rows]
+        self.row_req = torch.as_tensor(rr).to(device)
+        self.rows = int(rows)
+        p64 = np.asarray(p, np.int64)
+        K64 = np.asarray(K, np.int64)
+        self.W_max = int((p64 + K64 * self.L).max()) if len(p64) else self.L
+        n = self.rows_cap
+        i32, u8, f32 = torch.int32, torch.uint8, torch.float32
+        self.box_ids = torch.empty(n * self.W_max, dtype=i32, device=device)
+        self.box_valid = torch.empty(n * self.W_max, dtype=u8, device=device)
+        self.box_pos = torch.empty(n * self.W_max, dtype=i32, device=device)
+        self.masks = [torch.zeros(n * self.L, dtype=u8, device=device) for _ in range(2)]
+        self.cur = 0
+        self.tau = torch.empty(n, dtype=f32, device=device)
+        self.p_rows = torch.empty(n, dtype=i32, device=device)
+        self.b_rows = torch.empty(n, dtype=i32, device=device)
+        self.done = torch.zeros(n, dtype=u8, device=device)
+        self.accept = torch.zeros(n, dtype=i32, device=device)
+        self.conf = torch.empty(n * self.L, dtype=f32, device=device)
+        self.argmax = torch.empty(n * self.L, dtype=i32, device=device)
+        self.workspace = api.new_workspace(n, self.L, self.V, dtype, device=device)
+        self.status = torch.zeros(1, dtype=i32, device=device)
+        self.meta = torch.zeros(32, dtype=u8, device=device)
+        self.logits = logits if logits is not None else torch.empty((n, self.L, self.V), dtype=dtype, device=device)
+        self.W = 0
+        self.stats = dict(steps=0, positions_scored=0, compacts=0, packs=0, idle_request_steps=0, max_cost=0,
+                          evicted=0, admitted=0)
+        self.step_events = []          # (start, end) cuda events of each dllm_step, when timing
+
+    @classmethod
+    def from_workload(cls, w, device="cuda", logits=None):
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        return cls(w.p, w.K, w.b, w.state, w.threshold, w.arena_off, w.arena, w.blk_mask, w.row_req, w.rows,
+                   w.queue, L=w.L, V=w.V, dtype=dt, rows_cap=w.rows_cap, budget=w.budget, mask_id=w.mask_id,
+                   pad_id=w.pad_id, device=device, logits=logits)
+
+    # ---- views of the current box -------------------------------------------------------------
+    def box(self):
+        return self.box_ids[:self.rows * self.W].view(self.rows, self.W)
+
+    def mask(self):
+        return self.masks[self.cur][:self.rows * self.L].view(self.rows, self.L)
+
+    def check_status(self, where):
+        s = int(self.status.item())
+        if s != 0:
+            raise api.DllmError(s, where, "(device status)")
+
+    # ---- the three library calls ----------------------------------------------------------------
+    def compact(self, with_box=True):
+        kw = {}
+        if with_box and self.rows > 0:
+            kw = dict(box_ids=self.box_ids, mask=self.masks[self.cur], done=self.done)
+        api.dllm_compact(self.rows, self.L, self.W, self.mask_id, self.eos_id, self.row_req, self.rows_cap, self.reqs,
+                         self.queue, self.budget, self.meta, self.status, **kw)
+        m = api.read_meta(self.meta)
+        self.check_status("dllm_compact")
+        self.rows, self.W = m["rows"], m["W"]
+        self.stats["compacts"] += 1
+        self.stats["evicted"] += m["n_evicted"]
+        self.stats["admitted"] += m["n_admitted"]
+        self.stats["max_cost"] = max(self.stats["max_cost"], m["cost"])
+        return m
+
+    def pack(self):
+        api.dllm_pack(self.rows, self.L, self.W, self.pad_id, self.row_req, self.reqs, self.box_ids,
+                      self.masks[self.cur], self.tau, self.p_rows, self.b_rows, self.status, box_valid=self.box_valid,
+                      box_pos=self.box_pos)
+        self.stats["packs"] += 1
+
+    def step(self, timed=False):
+        nxt = 1 - self.cur
+        ev = None
+        if timed:
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ev[0].record()
+        api.dllm_step(self.logits, self.box(), self.masks[self.cur], self.masks[nxt], self.tau, self.done,
+                      self.accept, self.workspace, self.status, p=self.p_rows, b=self.b_rows, conf=self.conf,
+                      argmax=self.argmax, rows=self.rows, L=self.L, V=self.V, pos_stride=self.V,
+                      row_stride=self.L * self.V)
+        if timed:
+            ev[1].record()
+            self.step_events.append(ev)
+        self.cur = nxt
+
+    # ---- the loop rule ----------------------------------------------------------------------------
+    def run(self, mode, forward, max_steps=10**7, on_step=None, timed=False):
+        """Drive compact -> pack -> (forward, step)* -> compact ... until queue and rows are empty.
+
+        forward(session) fills session.logits for the current box.  on_step(session, info) is
+        called after every step with the host copies (done, new mask) — the test harness uses it
+        to check each step.  Returns self.stats."""
+        assert mode in ("sync", "fdfo")
+        self.compact(with_box=False)                 # admission at the start of the run
+        while self.rows > 0:
+            self.pack()
+            mask_host = self.mask().cpu().numpy()
+            while True:
+                if self.stats["steps"] >= max_steps:
+                    raise RuntimeError("step limit reached")
+                masked_rows = (mask_host != 0).any(axis=1)
+                self.stats["idle_request_steps"] += int((~masked_rows).sum())
+                self.stats["positions_scored"] += int((mask_host != 0).sum())
+                forward(self)
+                self.step(timed=timed)
+                done = self.done[:self.rows].cpu().numpy()
+                mask_host = self.mask().cpu().numpy()
+                self.check_status("dllm_step")
+                self.stats["steps"] += 1
+                if on_step is not None:
+                    on_step(self, dict(done=done, mask=mask_host))
+                if mode == "fdfo" and done.any():
+                    break
+                if mode == "sync" and done.all():
+                    break
+            self.compact(with_box=True)
+        return self.stats
+
+    # ---- host views for tests -----------------------------------------------------------------
+    def host_table(self):
+        """Host copies of the request table, row map and queue."""
+        torch.cuda.synchronize()
+        r = self.reqs
+        qlen = int(self.queue.len.item())
+        return dict(p=r.p.cpu().numpy(), K=r.K.cpu().numpy(), b=r.b.cpu().numpy(), state=r.state.cpu().numpy(),
+                    threshold=r.threshold.cpu().numpy(), arena_off=r.arena_off.cpu().numpy(),
+                    arena=r.arena.cpu().numpy(), blk_mask=r.blk_mask.cpu().numpy(),
+                    row_req=self.row_req.cpu().numpy(), queue=self.queue.ids[:qlen].cpu().numpy())

@@ -1,0 +1,137 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared symbol, sizes its
+workspace, and rejects bad arguments synchronously before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from confidence_block_unmasking_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(dllm_\w+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    declared = _declared()
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_workspace_bytes():
+    L = _lib.lib()
+    # V = 152064 bf16: 19008 vectors of 8, 38 chunks of <= 512 vectors
+    pos = 64 * 32
+    part = pos * 38 * 16
+    n = L.dllm_step_workspace_bytes(64, 32, 152064, _lib.DLLM_BF16)
+    assert n >= part + 3 * pos * 4 + 64 * 4 and n % 256 == 0
+    assert L.dllm_step_workspace_bytes(-1, 32, 1024, 0) == 0
+    assert L.dllm_step_workspace_bytes(4, 0, 1024, 0) == 0
+    assert L.dllm_step_workspace_bytes(4, 32, 1024, 9) == 0
+    # fp32 V = 1024: 256 vectors, one chunk
+    assert L.dllm_step_workspace_bytes(4, 32, 1024, _lib.DLLM_FP32) >= 128 * 16
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def _step(**kw):
+    a = dict(stream=None, logits=FAKE, dtype=1, pos_stride=1024, row_stride=32 * 1024, rows=4, L=32, V=1024,
+             ids=FAKE, W=64, mask_in=FAKE, mask_out=ctypes.c_void_p(0x2000), tau=FAKE, p=None, b=None, conf=None,
+             arg=None, done=FAKE, accept=FAKE, ws=FAKE, ws_bytes=0, status=FAKE)
+    a.update(kw)
+    return _lib.lib().dllm_step(a["stream"], a["logits"], a["dtype"], a["pos_stride"], a["row_stride"], a["rows"],
+                                a["L"], a["V"], a["ids"], a["W"], a["mask_in"], a["mask_out"], a["tau"], a["p"],
+                                a["b"], a["conf"], a["arg"], a["done"], a["accept"], a["ws"], a["ws_bytes"],
+                                a["status"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), _lib.DLLM_ERR_DTYPE),
+    (dict(rows=-1), _lib.DLLM_ERR_ARG),
+    (dict(L=0), _lib.DLLM_ERR_SHAPE),
+    (dict(L=1025, W=2000, row_stride=1025 * 1024), _lib.DLLM_ERR_SHAPE),
+    (dict(V=0), _lib.DLLM_ERR_ARG),
+    (dict(W=31), _lib.DLLM_ERR_SHAPE),
+    (dict(rows=4097), _lib.DLLM_ERR_SHAPE),
+    (dict(rows=4096, L=128, row_stride=128 * 1024, W=200), _lib.DLLM_ERR_SHAPE),
+    (dict(pos_stride=1000), _lib.DLLM_ERR_ARG),
+    (dict(row_stride=1024), _lib.DLLM_ERR_ARG),
+    (dict(p=FAKE), _lib.DLLM_ERR_ARG),
+    (dict(logits=None), _lib.DLLM_ERR_ARG),
+    (dict(status=None), _lib.DLLM_ERR_ARG),
+    (dict(mask_out=FAKE), _lib.DLLM_ERR_ARG),               # aliases mask_in
+    (dict(ws_bytes=10), _lib.DLLM_ERR_ARG),                 # workspace too small
+])
+def test_step_rejects_bad_arguments(kw, code):
+    assert _step(**kw) == code
+    assert _lib.last_error() != ""
+
+
+def test_step_rows_zero_is_noop():
+    assert _step(rows=0, logits=None, ids=None) == _lib.DLLM_OK
+
+
+def test_step_rejects_misaligned_workspace():
+    L = _lib.lib()
+    need = L.dllm_step_workspace_bytes(4, 32, 1024, 1)
+    assert _step(ws=ctypes.c_void_p(0x1004), ws_bytes=need) == _lib.DLLM_ERR_ARG
+
+
+def _reqs():
+    return _lib.Reqs(4, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+
+
+def test_pack_rejects_bad_arguments():
+    L = _lib.lib()
+    r = _reqs()
+    f = FAKE
+    assert L.dllm_pack(None, -1, 32, 64, 0, f, ctypes.byref(r), f, None, None, f, f, f, f, f) == _lib.DLLM_ERR_ARG
+    assert L.dllm_pack(None, 2, 0, 64, 0, f, ctypes.byref(r), f, None, None, f, f, f, f, f) == _lib.DLLM_ERR_SHAPE
+    assert L.dllm_pack(None, 2, 32, 16, 0, f, ctypes.byref(r), f, None, None, f, f, f, f, f) == _lib.DLLM_ERR_SHAPE
+    assert L.dllm_pack(None, 5000, 32, 64, 0, f, ctypes.byref(r), f, None, None, f, f, f, f, f) == _lib.DLLM_ERR_SHAPE
+    assert L.dllm_pack(None, 2, 32, 64, 0, None, ctypes.byref(r), f, None, None, f, f, f, f, f) == _lib.DLLM_ERR_ARG
+    bad = _lib.Reqs(4, 0x1000, 0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    assert L.dllm_pack(None, 2, 32, 64, 0, f, ctypes.byref(bad), f, None, None, f, f, f, f, f) == _lib.DLLM_ERR_ARG
+    assert L.dllm_pack(None, 0, 32, 0, 0, None, None, None, None, None, None, None, None, None, None) == _lib.DLLM_OK
+
+
+def test_compact_rejects_bad_arguments():
+    L = _lib.lib()
+    r = _reqs()
+    q = _lib.Queue(0x1000, 0x1000, 4)
+    f = FAKE
+
+    def call(rows=2, Lb=32, W=64, box=f, mask=f, done=f, row_req=f, cap=4, reqs=r, queue=q, meta=f, status=f):
+        return L.dllm_compact(None, rows, Lb, W, 0, -1, box, mask, done, row_req, cap,
+                              ctypes.byref(reqs) if reqs is not None else None,
+                              ctypes.byref(queue) if queue is not None else None, 0, meta, status)
+    assert call(rows=-1) == _lib.DLLM_ERR_ARG
+    assert call(rows=5, cap=4) == _lib.DLLM_ERR_ARG
+    assert call(cap=5000) == _lib.DLLM_ERR_SHAPE
+    assert call(Lb=0) == _lib.DLLM_ERR_SHAPE
+    assert call(mask=None) == _lib.DLLM_ERR_ARG
+    assert call(W=16) == _lib.DLLM_ERR_SHAPE
+    assert call(meta=None) == _lib.DLLM_ERR_ARG
+    assert call(queue=_lib.Queue(0x1000, 0x1000, 9000)) == _lib.DLLM_ERR_CAPACITY
+    assert call(queue=_lib.Queue(0x1000, None, 4)) == _lib.DLLM_ERR_ARG
+    bad = _lib.Reqs(4, 0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    assert call(reqs=bad) == _lib.DLLM_ERR_ARG
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _lib.lib()

@@ -1,0 +1,258 @@
+"""GPU parity of dllm_step against the float64 oracle (element by element), through the C ABI."""
+import numpy as np
+import pytest
+
+from oracle import pack as opack
+from oracle import step as ostep
+from tests.parity import CONF_TOL, check_decisions, check_scores
+from workload import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import confidence_block_unmasking_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _to_dev_logits(host, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(host).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(host)).cuda()
+
+
+def gpu_step(logits_host, dtype, ids, mask, tau, p=None, b=None, pos_stride=None, row_stride=None, ws=None,
+             offset=0):
+    """Run dllm_step on host inputs; logits may be embedded in a larger strided buffer."""
+    from confidence_block_unmasking_amd import api
+    rows, L, V = logits_host.shape
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    if pos_stride is None and row_stride is None and offset == 0:
+        lg = _to_dev_logits(logits_host, dtype)
+        ps, rs = V, L * V
+        base = lg
+    else:
+        ps = pos_stride or V
+        rs = row_stride or L * ps
+        total = offset + (rows - 1) * rs + (L - 1) * ps + V
+        buf = np.full(total, 0x7FC0 if dtype == "bf16" else np.nan,
+                      np.uint16 if dtype == "bf16" else np.float32)
+        for r in range(rows):
+            for j in range(L):
+                s = offset + r * rs + j * ps
+                buf[s:s + V] = logits_host[r, j]
+        dev = _to_dev_logits(buf, dtype)
+        base = dev[offset:]
+    W = ids.shape[1]
+    d_ids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    d_mask = torch.from_numpy(mask.astype(np.uint8)).cuda()
+    d_mask_out = torch.full_like(d_mask, 77)
+    d_tau = torch.from_numpy(np.asarray(tau, np.float32)).cuda()
+    done = torch.full((rows,), 9, dtype=torch.uint8, device="cuda")
+    acc = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+    conf = torch.full((rows, L), 5.0, dtype=torch.float32, device="cuda")
+    arg = torch.full((rows, L), -9, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if ws is None:
+        ws = api.new_workspace(rows, L, V, tdt)
+    kw = {}
+    if p is not None:
+        kw = dict(p=torch.from_numpy(np.asarray(p, np.int32)).cuda(), b=torch.from_numpy(np.asarray(b, np.int32)).cuda())
+    api.dllm_step(base, d_ids, d_mask, d_mask_out, d_tau, done, acc, ws, status, conf=conf, argmax=arg, rows=rows,
+                  L=L, V=V, pos_stride=ps, row_stride=rs, **kw)
+    torch.cuda.synchronize()
+    return dict(ids=d_ids.cpu().numpy(), mask=d_mask_out.cpu().numpy(), done=done.cpu().numpy(),
+                accept=acc.cpu().numpy(), conf=conf.cpu().numpy(), argmax=arg.cpu().numpy(),
+                status=int(status.item()), mask_in_after=d_mask.cpu().numpy())
+
+
+def check_step(logits, dtype, ids, mask, tau, g, p=None, b=None):
+    """Full element-by-element comparison of one GPU step with the oracle."""
+    o = ostep.step(logits, dtype, ids, mask, tau, p, b)
+    assert np.array_equal(g["mask_in_after"], mask), "mask_in was modified"
+    err = check_scores(g["conf"], g["argmax"], o["conf"], o["argmax"])
+    unscored = o["argmax"] < 0
+    assert np.all(g["argmax"][unscored] == -1) and np.all(g["conf"][unscored] == -1.0)
+    n_amb = check_decisions(g["conf"], o["conf"], mask, g["mask"], tau)
+    # lockstep: the oracle's write-back with the GPU's decisions must give identical integers
+    lk = ostep.step(logits, dtype, ids, mask, tau, conf_override=g["conf"].astype(np.float64))
+    for k in ("ids", "mask", "done", "accept"):
+        assert np.array_equal(g[k], lk[k]), k
+    if n_amb == 0:
+        for k in ("ids", "mask", "done", "accept"):
+            assert np.array_equal(g[k], o[k]), k
+    return err, n_amb
+
+
+def _packed_step_inputs(w):
+    W = opack.box_width(w.row_req, w.rows, w.p, w.b, w.L)
+    pk = opack.pack(w.row_req, w.rows, w.L, W, w.pad_id, w.p, w.b, w.threshold, w.arena_off, w.arena, w.blk_mask)
+    logits = synth.logits_cpu(w.rows, w.L, w.V, w.dtype, w.row_req, pk["b"], pk["mask"], w.logit_seed, w.sigma, w.umax)
+    return pk, logits
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_step_parity_configs(cfg):
+    w = configs.make(cfg)
+    pk, logits = _packed_step_inputs(w)
+    print(f"config {cfg}: rows={w.rows} L={w.L} V={w.V} masked={int(pk['mask'].sum())}", flush=True)
+    g = gpu_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"], pk["p"], pk["b"])
+    assert g["status"] == 0
+    err, n_amb = check_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"], g, pk["p"], pk["b"])
+    print(f"config {cfg}: max conf error {err:.3g}, ambiguous rows {n_amb}")
+    assert np.array_equal(g["ids"][:, :-w.L], pk["box_ids"][:, :-w.L])        # prompt columns untouched
+
+
+def test_generator_gpu_matches_cpu():
+    from confidence_block_unmasking_amd import api  # noqa: F401
+    for cfg in (1, 3):
+        w = configs.make(cfg)
+        rows = min(w.rows, 8)
+        rr = w.row_req[:rows]
+        blk = w.b[rr].astype(np.int32)
+        msk = w.blk_mask[rr]
+        host = synth.logits_cpu(rows, w.L, w.V, w.dtype, rr, blk, msk, w.logit_seed, w.sigma, w.umax, fill_nan=True)
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        dev = torch.empty((rows, w.L, w.V), dtype=tdt, device="cuda")
+        synth.logits_gpu(dev, w.dtype, rows, w.L, w.V, torch.from_numpy(rr.astype(np.int32)).cuda(),
+                         torch.from_numpy(blk).cuda(), torch.from_numpy(msk).cuda(), w.logit_seed, w.sigma, w.umax,
+                         fill_nan=True)
+        torch.cuda.synchronize()
+        got = dev.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else dev.cpu().numpy()
+        if w.dtype == "bf16":
+            assert np.array_equal(got, host)
+        else:
+            assert np.array_equal(got.view(np.uint32), host.view(np.uint32))
+
+
+def _rand_case(rng, rows, L, V, dtype, p_mask=0.5, W_extra=3, scale=2.0, planted=12.0):
+    x = rng.normal(0, scale, (rows, L, V)).astype(np.float32)
+    for r in range(rows):
+        for j in range(L):
+            x[r, j, rng.integers(0, V)] += rng.uniform(0, planted)
+    if dtype == "bf16":
+        u = x.view(np.uint32).astype(np.uint64)
+        logits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    else:
+        logits = x
+    W = L + W_extra
+    ids = rng.integers(0, V, (rows, W)).astype(np.int32)
+    mask = (rng.random((rows, L)) < p_mask).astype(np.uint8)
+    tau = rng.choice([0.5, 0.6, 0.7, 0.8, 0.9], rows).astype(np.float32)
+    return logits, ids, mask, tau
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("rows,L,V", [(1, 1, 1), (3, 5, 7), (2, 32, 1000), (2, 32, 1001), (4, 64, 4099),
+                                      (2, 100, 515), (1, 7, 65536), (5, 33, 8200)])
+def test_step_shapes_and_ragged_tails(dtype, rows, L, V):
+    rng = np.random.default_rng(rows * 1000 + L * 10 + V)
+    logits, ids, mask, tau = _rand_case(rng, rows, L, V, dtype)
+    mask[0, 0] = 1
+    print(f"shape rows={rows} L={L} V={V} {dtype}", flush=True)
+    g = gpu_step(logits, dtype, ids, mask, tau)
+    assert g["status"] == 0
+    check_step(logits, dtype, ids, mask, tau, g)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_step_strided_and_unaligned(dtype):
+    rng = np.random.default_rng(17)
+    rows, L, V = 3, 6, 2051
+    logits, ids, mask, tau = _rand_case(rng, rows, L, V, dtype)
+    for ps, rs, off in [(V + 5, None, 0), (V, L * V + 3, 1), (2056, 2056 * L + 8, 8)]:
+        print(f"strides pos={ps} row={rs} offset={off}", flush=True)
+        g = gpu_step(logits, dtype, ids, mask, tau, pos_stride=ps, row_stride=rs, offset=off)
+        check_step(logits, dtype, ids, mask, tau, g)
+
+
+def test_step_mask_patterns_and_ties():
+    rows, L, V = 6, 8, 300
+    logits = np.zeros((rows, L, V), np.float32)
+    logits[1, :, 17] = 3.0                      # same value at one index: ties across slots
+    logits[2, :, 5] = 9.0
+    logits[2, :, 200] = 9.0                     # tie inside a row of the vocabulary: lowest index wins
+    logits[3, 2, 10] = 50.0                     # one very confident slot
+    logits[4] = np.random.default_rng(3).normal(0, 1, (L, V))
+    ids = np.arange(rows * (L + 2), dtype=np.int32).reshape(rows, L + 2)
+    mask = np.ones((rows, L), np.uint8)
+    mask[0] = 0                                 # nothing masked: done, accept = L, untouched
+    mask[5] = 0
+    mask[5, 7] = 1                              # a single masked slot: the fallback finishes the block
+    tau = np.array([0.9, 0.9, 0.4, 0.9, 0.99, 0.9], np.float32)
+    g = gpu_step(logits, "fp32", ids, mask, tau)
+    check_step(logits, "fp32", ids, mask, tau, g)
+    assert g["done"].tolist() == [1, 0, 1, 0, 0, 1]           # row 2: every slot clears tau = 0.4
+    assert g["accept"].tolist() == [L, 0, L, 0, 0, L]
+    assert np.all(g["argmax"][2] == 5)
+    assert g["mask"][3].tolist() == [1, 1, 0, 1, 1, 1, 1, 1]     # only the confident slot
+    assert g["mask"][1].sum() == L - 1 and g["mask"][1, 0] == 0   # fallback tie across slots -> slot 0
+    assert np.array_equal(g["ids"][0], ids[0])
+
+
+def test_step_threshold_equal_is_not_above():
+    # two slots with softmax confidence exactly 0.5 (logits (0, 0) over V = 2) and tau = 0.5
+    logits = np.zeros((1, 2, 2), np.float32)
+    ids = np.zeros((1, 2), np.int32)
+    mask = np.ones((1, 2), np.uint8)
+    g = gpu_step(logits, "fp32", ids, mask, np.array([0.5], np.float32))
+    assert g["conf"][0].tolist() == [0.5, 0.5]
+    assert g["mask"][0].tolist() == [0, 1]      # no slot exceeds: fallback to the lowest slot
+
+
+def test_step_many_chunks_merge_path():
+    # V large enough for more than 64 chunks per slot (the multi-block merge)
+    rng = np.random.default_rng(8)
+    logits, ids, mask, tau = _rand_case(rng, 1, 3, 300000, "bf16", p_mask=1.0)
+    logits[0, 1, 299999] = 0x4200                 # max at the very last element
+    g = gpu_step(logits, "bf16", ids, mask, tau)
+    check_step(logits, "bf16", ids, mask, tau, g)
+
+
+def test_step_never_reads_unmasked_slots():
+    w = configs.config1()
+    pk, logits = _packed_step_inputs(w)           # unmasked slots hold NaN
+    assert np.isnan(logits[pk["mask"] == 0]).all()
+    g = gpu_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"])
+    assert np.all(np.isfinite(g["conf"]))
+    check_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"], g)
+
+
+def test_step_status_for_row_that_does_not_fit():
+    rng = np.random.default_rng(2)
+    logits, ids, mask, tau = _rand_case(rng, 2, 4, 64, "fp32", W_extra=2)
+    g = gpu_step(logits, "fp32", ids, mask, tau, p=[2, 3], b=[0, 0])   # row 1 needs 7 > W = 6
+    assert g["status"] == 2
+    check_step(logits, "fp32", ids, mask, tau, g)                      # the step still completes
+
+
+def test_step_determinism_and_batch_invariance():
+    w = configs.config3()
+    pk, logits = _packed_step_inputs(w)
+    a = gpu_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"])
+    b = gpu_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"])
+    for k in a:
+        assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+    # the same rows in another order, with half of the batch removed: identical bits per row
+    rng = np.random.default_rng(4)
+    sel = rng.permutation(w.rows)[:w.rows // 2]
+    c = gpu_step(logits[sel], w.dtype, pk["box_ids"][sel], pk["mask"][sel], pk["threshold"][sel])
+    for k in ("ids", "mask", "done", "accept", "argmax"):
+        assert np.array_equal(c[k], a[k][sel]), k
+    assert np.array_equal(c["conf"].view(np.uint32), a["conf"][sel].view(np.uint32))
+
+
+def test_workspace_reused_across_shapes():
+    from confidence_block_unmasking_amd import api
+    rng = np.random.default_rng(6)
+    ws = api.new_workspace(64, 64, 70000, torch.bfloat16)
+    for rows, L, V in [(5, 16, 70000), (64, 64, 3000), (2, 3, 65000), (17, 40, 9000)]:
+        logits, ids, mask, tau = _rand_case(rng, rows, L, V, "bf16", p_mask=0.7)
+        g = gpu_step(logits, "bf16", ids, mask, tau, ws=ws)
+        check_step(logits, "bf16", ids, mask, tau, g)
+        assert int(torch.count_nonzero(ws).item()) == 0          # every used byte returned to zero
+    assert CONF_TOL == 1e-5
