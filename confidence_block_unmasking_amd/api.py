@@ -43,7 +43,7 @@ def dllm_step_workspace_bytes(rows: int, L: int, V: int, dtype=torch.bfloat16) -
 
 
 def new_workspace(rows: int, L: int, V: int, dtype=torch.bfloat16, device="cuda"):
-    """A zero-filled step workspace (zeroed once; every call leaves it zeroed)."""
+    """A step workspace for this shape (the step needs no particular contents; zero-filled here)."""
     n = dllm_step_workspace_bytes(rows, L, V, dtype)
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 

@@ -31,7 +31,7 @@ extern "C" {
 
 typedef enum {
     DLLM_OK = 0,
-    DLLM_ERR_ARG = 1,       /* null pointer, bad size, aliasing, workspace too small */
+    DLLM_ERR_ARG = 1,       /* null pointer, bad size or id, workspace too small */
     DLLM_ERR_SHAPE = 2,     /* shape outside the supported limits, or a row that does not fit the box */
     DLLM_ERR_DTYPE = 3,     /* unknown logits dtype */
     DLLM_ERR_CAPACITY = 4,  /* a queued request cannot be admitted even into an empty batch; queue too long */
@@ -106,20 +106,22 @@ typedef struct {
  *              fp32 or bf16; must be finite.  Only masked slots are read.  16-byte aligned rows
  *              (base and both strides) take the vector path; others a slower element path.
  * input_ids  : int32 [rows, W], row-major; only active-block columns of unmasked slots are written.
- * mask_in    : uint8 [rows, L]; mask_out: uint8 [rows, L], every entry written; must not alias mask_in.
+ * mask_in    : uint8 [rows, L]; mask_out: uint8 [rows, L], every entry written; may be mask_in
+ *              itself (in-place update), but must not overlap it otherwise.
  * threshold  : float32 [rows].   p, b: int32 [rows] or both NULL; when given, a row with
  *              p + (b + 1) L > W sets *status = DLLM_ERR_SHAPE (the step still completes).
  * conf, argmax: float32 / int32 [rows, L] outputs, or NULL; -1 where a slot was not scored.
  * done       : uint8 [rows]; accept_len: int32 [rows].
- * workspace  : device memory of at least dllm_step_workspace_bytes(rows, L, V, dtype) bytes,
- *              16-byte aligned, ZERO-FILLED before its first use; every call returns every
- *              byte it used to zero, so it is zeroed once per allocation and may serve calls of
- *              any shape that fits it.  Not shared by overlapping calls.
+ * workspace  : device scratch of at least dllm_step_workspace_bytes(rows, L, V, dtype) bytes,
+ *              16-byte aligned, any contents: it holds per-chunk partial results, each written
+ *              before it is read.  Serves calls of any shape that fits.  Not shared by
+ *              overlapping calls.
  * status     : device int32 (see conventions).
- * Errors: DLLM_ERR_ARG (null required pointer, rows < 0, V < 1, strides too small, aliasing,
- * workspace too small or misaligned), DLLM_ERR_SHAPE (L outside [1, DLLM_MAX_L], W < L,
+ * Errors: DLLM_ERR_ARG (null required pointer, rows < 0, V < 1, strides too small, mask_out
+ * overlapping mask_in without being it, workspace too small or misaligned), DLLM_ERR_SHAPE (L outside [1, DLLM_MAX_L], W < L,
  * rows > DLLM_MAX_ROWS, rows*L > DLLM_MAX_POSITIONS), DLLM_ERR_DTYPE, DLLM_ERR_HIP.
- * rows == 0 is a no-op returning DLLM_OK. */
+ * rows == 0 is a no-op returning DLLM_OK.  Work: two kernels on `stream` (scoring, then the
+ * per-row decision); the call returns after enqueueing both. */
 dllm_status dllm_step(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
                       int64_t row_stride, int32_t rows, int32_t L, int32_t V, int32_t *input_ids,
                       int32_t W, const uint8_t *mask_in, uint8_t *mask_out, const float *threshold,

@@ -35,7 +35,7 @@ def test_workspace_bytes():
     pos = 64 * 32
     part = pos * 38 * 16
     n = L.dllm_step_workspace_bytes(64, 32, 152064, _lib.DLLM_BF16)
-    assert n >= part + 3 * pos * 4 + 64 * 4 and n % 256 == 0
+    assert n >= part and n % 256 == 0
     assert L.dllm_step_workspace_bytes(-1, 32, 1024, 0) == 0
     assert L.dllm_step_workspace_bytes(4, 0, 1024, 0) == 0
     assert L.dllm_step_workspace_bytes(4, 32, 1024, 9) == 0
@@ -71,7 +71,7 @@ def _step(**kw):
     (dict(p=FAKE), _lib.DLLM_ERR_ARG),
     (dict(logits=None), _lib.DLLM_ERR_ARG),
     (dict(status=None), _lib.DLLM_ERR_ARG),
-    (dict(mask_out=FAKE), _lib.DLLM_ERR_ARG),               # aliases mask_in
+    (dict(mask_out=ctypes.c_void_p(0x1000 + 127)), _lib.DLLM_ERR_ARG),   # overlaps mask_in's last byte
     (dict(ws_bytes=10), _lib.DLLM_ERR_ARG),                 # workspace too small
 ])
 def test_step_rejects_bad_arguments(kw, code):
