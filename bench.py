@@ -4,18 +4,26 @@
 Workload: the Dream-shaped dynamic-threshold step — 64 requests at block 0, block length L = 32,
 vocabulary V = 152064, bf16 logits (noise sd 2 plus one planted token per slot, offset U[0,14]),
 per-request thresholds drawn from {0.5, 0.6, 0.7, 0.8, 0.9}, masked fraction U[0.1, 1.0] per block.
-One timed step is the whole device path for one batch: dllm_pack (box gather), dllm_step (score
-every masked slot, LowConfidence decision, write-back) and dllm_compact (scatter, commit, evict).
-Every step starts from its own pristine copy of the request state, and the logits rotate over
-several device buffers (more bytes than the 256 MB Infinity Cache), all resident before timing.
+One timed step is the whole device path for one batch: dllm_pack (box gather), dllm_step_score
+(every masked slot's vocabulary row), dllm_step_decide (LowConfidence decision and write-back) and
+dllm_compact (scatter, commit, evict).  Every step starts from its own pristine copy of the request
+state, and the logits rotate over several device buffers (more bytes than the 256 MB Infinity
+Cache), all resident in HBM before timing.
 
-Reports masked positions scored per second over the timed region, the dllm_step kernel's HBM
-roofline fraction from per-launch HIP events, and the float64 oracle's rate on the host cores.
+Reports masked positions scored per second over the timed region, the HBM roofline fraction of
+the scoring kernel (the dominant one) from HIP events on the launch stream, and the float64
+oracle's rate on the host cores (run first, before the GPU is touched).
+
+Other modes: --copy-calibration MIB runs only a plain device copy (for scaling the HBM byte
+counters); --record-traffic turns rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the stored traffic
+figure that later runs report.
 """
 import argparse
 import ctypes
+import glob
 import hashlib
 import json
+import multiprocessing as mp
 import os
 import sys
 import time
@@ -25,14 +33,69 @@ sys.path.insert(0, ROOT)
 
 METRIC = "masked positions scored/sec + logits HBM GB/s (fraction of MI355X peak), 1 GPU"
 PEAK_HBM_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dllm_step_dream_dynamic_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_dream_dynamic_traffic.json")
 STEP_SRC = os.path.join(ROOT, "confidence_block_unmasking_amd", "csrc", "step.hip")
+SCORE_KERNEL = "score_kernel"
+COPY_MIB = 256
 
 
 def _sha(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
+
+# ---- CPU baseline: the float64 oracle as it stands, on host cores ------------------------------
+
+_CPU = {}
+
+
+def _cpu_worker(args):
+    rows_mine, seconds = args
+    from oracle import step as ostep
+    d = _CPU
+    slots, t0 = 0, time.perf_counter()
+    while True:
+        for r in rows_mine:
+            ostep.step(d["logits"][r:r + 1], d["dtype"], d["ids"][r:r + 1], d["mask"][r:r + 1], d["tau"][r:r + 1])
+            slots += d["nmask"][r]
+            if time.perf_counter() - t0 >= seconds:
+                return slots, time.perf_counter() - t0
+
+
+def cpu_baseline(cpu_seconds):
+    """The oracle's step on the same configuration, rows spread over a pool of host processes
+    (one thread each), for about `cpu_seconds` of CPU work in all.  Logits generation excluded."""
+    import numpy as np
+
+    from oracle import pack as opack
+    from workload import configs, synth
+    w = configs.config3()
+    W = opack.box_width(w.row_req, w.rows, w.p, w.b, w.L)
+    pk = opack.pack(w.row_req, w.rows, w.L, W, w.pad_id, w.p, w.b, w.threshold, w.arena_off, w.arena, w.blk_mask)
+    _CPU.update(logits=synth.logits_cpu(w.rows, w.L, w.V, w.dtype, w.row_req, pk["b"], pk["mask"], w.logit_seed,
+                                        w.sigma, w.umax),
+                dtype=w.dtype, ids=pk["box_ids"], mask=pk["mask"], tau=pk["threshold"],
+                nmask=[int(x) for x in pk["mask"].sum(1)])
+    n = max(1, min(16, os.cpu_count() or 1))
+    per = max(1.0, cpu_seconds / n)
+    parts = [list(range(k, w.rows, n)) for k in range(n)]
+    os.environ["OMP_NUM_THREADS"] = "1"
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(n) as pool:
+        res = pool.map(_cpu_worker, [(rp, per) for rp in parts if rp])
+    wall = time.perf_counter() - t0
+    slots = sum(s for s, _ in res)
+    busy = max(t for _, t in res)
+    _CPU.clear()
+    value = slots / busy
+    return {"value": value, "unit": "masked positions/s", "cores": len(res), "kind": "oracle",
+            "sample": f"{slots} masked-slot scorings of the same 64-row step (rows round-robin over {len(res)} "
+                      f"processes, one thread each, {per:.1f} s each, repeated passes; {wall:.1f} s wall); "
+                      "numpy float64; logits generation excluded",
+            "logits_GBps_equiv": value * w.V * w.elem_bytes / 1e9}
+
+
+# ---- HBM byte counters -------------------------------------------------------------------------
 
 def copy_calibration(mib):
     """A plain device copy of known size, for scaling the HBM byte counters."""
@@ -46,11 +109,73 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
+def _pmc_rows(d):
+    """(kernel name, counter, value) rows of a rocprofv3 --pmc run with CSV output under d."""
+    import csv
+    out = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                out.append((row.get("Kernel_Name", ""), row.get("Counter_Name", ""),
+                            float(row.get("Counter_Value", "nan")), row.get("Dispatch_Id", "")))
+    if not out:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return out
+
+
+def _per_dispatch(rows, kernel_pred, counter):
+    tot = {}
+    for name, cn, v, disp in rows:
+        if cn == counter and kernel_pred(name):
+            tot[disp] = tot.get(disp, 0.0) + v
+    if not tot:
+        raise SystemExit(f"no {counter} rows for the kernel")
+    vals = sorted(tot.values())
+    return vals[len(vals) // 2], len(vals)
+
+
+def record_traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, masked):
+    """Median KiB per dispatch of FETCH_SIZE and WRITE_SIZE for the scoring kernel, each scaled by
+    (known bytes / counted bytes) of a plain copy of COPY_MIB MiB; written to TRAFFIC_FILE."""
+    is_score = lambda n: SCORE_KERNEL in n  # noqa: E731
+    is_copy = lambda n: "copyBuffer" in n or "copy" in n.lower()  # noqa: E731
+    known_kib = COPY_MIB * 1024.0
+    f_kib, nf = _per_dispatch(_pmc_rows(fetch_dir), is_score, "FETCH_SIZE")
+    w_kib, nw = _per_dispatch(_pmc_rows(write_dir), is_score, "WRITE_SIZE")
+    cf_kib, _ = _per_dispatch(_pmc_rows(cfetch_dir), is_copy, "FETCH_SIZE")
+    cw_kib, _ = _per_dispatch(_pmc_rows(cwrite_dir), is_copy, "WRITE_SIZE")
+    sf, sw = known_kib / cf_kib, known_kib / cw_kib
+    rec = {"kernel": SCORE_KERNEL, "workload": "Dream-shaped dynamic-threshold step (64 x 32 x 152064 bf16)",
+           "masked_positions": masked, "source_sha256": _sha(STEP_SRC),
+           "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
+           "copy_mib": COPY_MIB, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
+           "fetch_scale": sf, "write_scale": sw,
+           "hbm_bytes_per_launch": (f_kib * sf + w_kib * sw) * 1024.0}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec), flush=True)
+
+
+def stored_traffic(masked):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        tr = json.load(f)
+    if tr.get("source_sha256") != _sha(STEP_SRC) or tr.get("masked_positions") != masked:
+        return None                       # the kernel changed since the counters were taken
+    return tr.get("hbm_bytes_per_launch")
+
+
+# ---- the timed device path ---------------------------------------------------------------------
+
 class _Copy:
     """Mutable request state of one timed step (the immutable fields are shared)."""
 
     def __init__(self, sess):
         import torch
+
+        from confidence_block_unmasking_amd import _lib
         r = sess.reqs
         self.b = r.b.clone()
         self.state = r.state.clone()
@@ -60,62 +185,17 @@ class _Copy:
         self.q_ids = sess.queue.ids.clone()
         self.q_len = sess.queue.len.clone()
         self.meta = torch.zeros(32, dtype=torch.uint8, device="cuda")
-        from confidence_block_unmasking_amd import _lib
         self.reqs = _lib.Reqs(r.n_req, r.p.data_ptr(), r.K.data_ptr(), self.b.data_ptr(), self.state.data_ptr(),
                               r.threshold.data_ptr(), r.arena_off.data_ptr(), self.arena.data_ptr(),
                               self.blk_mask.data_ptr())
         self.queue = _lib.Queue(self.q_ids.data_ptr(), self.q_len.data_ptr(), sess.queue.cap)
 
 
-def cpu_baseline(w, seconds):
-    """The float64 oracle, as it stands, on rows of the same workload until `seconds` have passed."""
-    import numpy as np
-
-    from oracle import pack as opack
-    from oracle import step as ostep
-    from workload import synth
-    W = opack.box_width(w.row_req, w.rows, w.p, w.b, w.L)
-    pk = opack.pack(w.row_req, w.rows, w.L, W, w.pad_id, w.p, w.b, w.threshold, w.arena_off, w.arena, w.blk_mask)
-    slots, elapsed, rows_done = 0, 0.0, 0
-    for r in range(w.rows):
-        lg = synth.logits_cpu(1, w.L, w.V, w.dtype, w.row_req[r:r + 1], pk["b"][r:r + 1], pk["mask"][r:r + 1],
-                              w.logit_seed, w.sigma, w.umax)
-        t0 = time.perf_counter()
-        ostep.step(lg, w.dtype, pk["box_ids"][r:r + 1], pk["mask"][r:r + 1], pk["threshold"][r:r + 1])
-        elapsed += time.perf_counter() - t0
-        slots += int(pk["mask"][r].sum())
-        rows_done += 1
-        if elapsed >= seconds:
-            break
-    return {"value": slots / elapsed, "unit": "masked positions/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows_done} of {w.rows} rows ({slots} masked slots, {elapsed:.1f} s), numpy float64, "
-                      "one thread; logits generation excluded",
-            "logits_GBps_equiv": slots * w.V * w.elem_bytes / elapsed / 1e9}
-
-
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--rotate", type=int, default=4, help="logits buffers cycled through")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of this many MiB (HBM counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); rows of the step "
-              "shard across GPUs without any exchange, but no multi-GPU path is built", file=sys.stderr)
-        sys.exit(2)
+def run_gpu(args):
     import numpy as np
     import torch
 
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-
-    from confidence_block_unmasking_amd import _lib, api
+    from confidence_block_unmasking_amd import _lib
     from confidence_block_unmasking_amd.driver import Session
     from workload import configs, synth
 
@@ -134,7 +214,8 @@ def main():
         t = torch.empty((rows, L, V), dtype=torch.bfloat16, device="cuda")
         synth.logits_gpu(t, w.dtype, rows, L, V, rr, bb, mm, w.logit_seed + 7919 * k, w.sigma, w.umax)
         bufs.append(t)
-    copies = [_Copy(sess) for _ in range(args.warmup + args.steps)]
+    n_total = args.warmup + args.steps
+    copies = [_Copy(sess) for _ in range(n_total)]
     torch.cuda.synchronize()
 
     lib = _lib.lib()
@@ -143,11 +224,12 @@ def main():
     box = sess.box_ids
     mask_a, mask_b = sess.masks
     P = lambda t: vp(t.data_ptr())  # noqa: E731
-    step_args = []
-    for k in range(args.rotate):
-        step_args.append((stream, P(bufs[k]), _lib.DLLM_BF16, V, L * V, rows, L, V, P(box), W, P(mask_a), P(mask_b),
-                          P(sess.tau), P(sess.p_rows), P(sess.b_rows), P(sess.conf), P(sess.argmax), P(sess.done),
-                          P(sess.accept), P(sess.workspace), sess.workspace.numel(), P(sess.status)))
+    ws, wsn = P(sess.workspace), sess.workspace.numel()
+    score_args = [(stream, P(bufs[k]), _lib.DLLM_BF16, V, L * V, rows, L, V, P(mask_a), ws, wsn, P(sess.status))
+                  for k in range(args.rotate)]
+    decide_args = (stream, _lib.DLLM_BF16, rows, L, V, P(box), W, P(mask_a), P(mask_b), P(sess.tau), P(sess.p_rows),
+                   P(sess.b_rows), P(sess.conf), P(sess.argmax), P(sess.done), P(sess.accept), ws, wsn,
+                   P(sess.status))
     pack_args, comp_args = [], []
     for c in copies:
         pack_args.append((stream, rows, L, W, w.pad_id, P(c.row_req), ctypes.byref(c.reqs), P(box),
@@ -156,14 +238,15 @@ def main():
         comp_args.append((stream, rows, L, W, w.mask_id, -1, P(box), P(mask_b), P(sess.done), P(c.row_req),
                           w.rows_cap, ctypes.byref(c.reqs), ctypes.byref(c.queue), w.budget, P(c.meta),
                           P(sess.status)))
-    n_total = args.warmup + args.steps
+    # HIP events on the launch stream (torch's current stream), around the scoring kernel only
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_total)]
 
     def one(k):
         rc = lib.dllm_pack(*pack_args[k])
         ev[k][0].record()
-        rc |= lib.dllm_step(*step_args[k % args.rotate])
+        rc |= lib.dllm_step_score(*score_args[k % args.rotate])
         ev[k][1].record()
+        rc |= lib.dllm_step_decide(*decide_args)
         rc |= lib.dllm_compact(*comp_args[k])
         return rc
 
@@ -178,21 +261,15 @@ def main():
     t1 = time.perf_counter()
     if rc != 0 or int(sess.status.item()) != 0:
         raise SystemExit(f"library error rc={rc} status={int(sess.status.item())}: {_lib.last_error()}")
-    # sanity: every timed step evicted the rows whose block completed, from the same start state
     metas = {bytes(c.meta.cpu().numpy()) for c in copies[args.warmup:]}
-    assert len(metas) >= 1
+    if len(metas) != 1:
+        raise SystemExit("timed steps from the same start state produced different layouts")
     elapsed = t1 - t0
     kern_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(args.warmup, n_total)])
     kern_s = float(kern_ms.mean()) / 1e3
     step_bytes = M * V * 2
     achieved = step_bytes / kern_s / 1e9
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("source_sha256") == _sha(STEP_SRC) and tr.get("masked_positions") == M:
-            traffic = tr.get("hbm_bytes_per_launch")
-    out = {
+    return {
         "metric": METRIC,
         "value": M * args.steps / elapsed,
         "unit": "masked positions/s",
@@ -206,18 +283,48 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "Dream-shaped dynamic-threshold step: 64 requests, L=32, V=152064 bf16 logits, "
-                               "thresholds {0.5..0.9}, masked fraction U[0.1,1.0]; step = pack + step + compact",
+                               "thresholds {0.5..0.9}, masked fraction U[0.1,1.0]; step = pack + score + decide + "
+                               "compact",
                    "requests": w.rows, "block_len": L, "vocab": V, "logits_dtype": "bf16",
                    "masked_positions_per_step": M, "box_width": W, "logits_buffers": args.rotate},
         "logits_GBps": step_bytes * args.steps / elapsed / 1e9,
-        "step_kernel_us": {"mean": float(kern_ms.mean()) * 1e3, "p10": float(np.percentile(kern_ms, 10)) * 1e3,
-                           "p50": float(np.percentile(kern_ms, 50)) * 1e3,
-                           "p90": float(np.percentile(kern_ms, 90)) * 1e3},
+        "score_kernel_us": {"mean": float(kern_ms.mean()) * 1e3, "p10": float(np.percentile(kern_ms, 10)) * 1e3,
+                            "p50": float(np.percentile(kern_ms, 50)) * 1e3,
+                            "p90": float(np.percentile(kern_ms, 90)) * 1e3},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic},
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": stored_traffic(M)},
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=4, help="logits buffers cycled through")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU work of the oracle baseline, in all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write the traffic file from four rocprofv3 --pmc CSV output folders (no GPU use)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); rows of the step "
+              "shard across GPUs without any exchange, but no multi-GPU path is built", file=sys.stderr)
+        sys.exit(2)
+    if args.record_traffic:
+        from workload import configs
+        w = configs.config3()
+        record_traffic(*args.record_traffic, masked=int(w.blk_mask[w.row_req[:w.rows]].sum()))
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)   # before the GPU is touched
+    out = run_gpu(args)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -48,14 +48,7 @@ def new_workspace(rows: int, L: int, V: int, dtype=torch.bfloat16, device="cuda"
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def dllm_step(logits, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status,
-              p=None, b=None, conf=None, argmax=None, rows=None, L=None, V=None, pos_stride=None,
-              row_stride=None, stream=None):
-    """One LowConfidence denoise step (see include/dllm.h).
-
-    logits: [rows, L, V] bf16/fp32 device tensor, or any tensor whose storage holds element
-    (r, j, v) at r*row_stride + j*pos_stride + v when the strides are given.
-    """
+def _logits_shape(logits, rows, L, V, pos_stride, row_stride):
     if logits.dtype not in _DT:
         raise ValueError(f"logits dtype {logits.dtype} not supported")
     if rows is None:
@@ -64,6 +57,11 @@ def dllm_step(logits, input_ids, mask_in, mask_out, threshold, done, accept_len,
         pos_stride = logits.stride(1) if logits.dim() == 3 else V
     if row_stride is None:
         row_stride = logits.stride(0) if logits.dim() == 3 else L * pos_stride
+    return rows, L, V, pos_stride, row_stride
+
+
+def _decide_args(rows, L, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status, p, b, conf,
+                 argmax):
     W = input_ids.shape[-1]
     _need(input_ids, torch.int32, "input_ids", rows * W)
     _need(mask_in, torch.uint8, "mask_in", rows * L)
@@ -77,11 +75,51 @@ def dllm_step(logits, input_ids, mask_in, mask_out, threshold, done, accept_len,
                          (conf, torch.float32, "conf", rows * L), (argmax, torch.int32, "argmax", rows * L)):
         if t is not None:
             _need(t, dt, nm, n)
+    return W
+
+
+def dllm_step(logits, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status,
+              p=None, b=None, conf=None, argmax=None, rows=None, L=None, V=None, pos_stride=None,
+              row_stride=None, stream=None):
+    """One LowConfidence denoise step (see include/dllm.h).
+
+    logits: [rows, L, V] bf16/fp32 device tensor, or any tensor whose storage holds element
+    (r, j, v) at r*row_stride + j*pos_stride + v when the strides are given.
+    """
+    rows, L, V, pos_stride, row_stride = _logits_shape(logits, rows, L, V, pos_stride, row_stride)
+    W = _decide_args(rows, L, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status, p, b,
+                     conf, argmax)
     rc = _lib.lib().dllm_step(_stream(stream), _ptr(logits), _DT[logits.dtype], pos_stride, row_stride, rows, L, V,
                               _ptr(input_ids), W, _ptr(mask_in), _ptr(mask_out), _ptr(threshold), _ptr(p), _ptr(b),
                               _ptr(conf), _ptr(argmax), _ptr(done), _ptr(accept_len), _ptr(workspace),
                               workspace.numel(), _ptr(status))
     _lib.check(rc, "dllm_step")
+
+
+def dllm_step_score(logits, mask_in, workspace, status, rows=None, L=None, V=None, pos_stride=None,
+                    row_stride=None, stream=None):
+    """The scoring half of dllm_step: per-chunk partials of every masked slot into `workspace`."""
+    rows, L, V, pos_stride, row_stride = _logits_shape(logits, rows, L, V, pos_stride, row_stride)
+    _need(mask_in, torch.uint8, "mask_in", rows * L)
+    _need(workspace, torch.uint8, "workspace")
+    _need(status, torch.int32, "status", 1)
+    rc = _lib.lib().dllm_step_score(_stream(stream), _ptr(logits), _DT[logits.dtype], pos_stride, row_stride, rows,
+                                    L, V, _ptr(mask_in), _ptr(workspace), workspace.numel(), _ptr(status))
+    _lib.check(rc, "dllm_step_score")
+
+
+def dllm_step_decide(dtype, rows, L, V, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status,
+                     p=None, b=None, conf=None, argmax=None, stream=None):
+    """The deciding half of dllm_step, on the partials dllm_step_score left in `workspace`
+    (same dtype, rows, L, V and mask_in)."""
+    if dtype not in _DT:
+        raise ValueError(f"dtype {dtype} not supported")
+    W = _decide_args(rows, L, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status, p, b,
+                     conf, argmax)
+    rc = _lib.lib().dllm_step_decide(_stream(stream), _DT[dtype], rows, L, V, _ptr(input_ids), W, _ptr(mask_in),
+                                     _ptr(mask_out), _ptr(threshold), _ptr(p), _ptr(b), _ptr(conf), _ptr(argmax),
+                                     _ptr(done), _ptr(accept_len), _ptr(workspace), workspace.numel(), _ptr(status))
+    _lib.check(rc, "dllm_step_decide")
 
 
 class ReqTable:

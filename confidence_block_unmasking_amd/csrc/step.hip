@@ -544,6 +544,110 @@ inline bool shape_of(int32_t rows, int32_t L, int32_t V, dllm_dtype dt, int &NV,
     return true;
 }
 
+// Checks shared by the three entry points; fills P's shape fields.  `who` names the caller.
+dllm_status check_shape(const char *who, dllm_dtype dtype, int32_t rows, int32_t L, int32_t V, void *workspace,
+                        StepParams &P) {
+    if (dtype != DLLM_FP32 && dtype != DLLM_BF16) return fail(DLLM_ERR_DTYPE, "%s: unknown dtype %d", who, (int)dtype);
+    if (rows < 0) return fail(DLLM_ERR_ARG, "%s: rows < 0", who);
+    if (L < 1 || L > DLLM_MAX_L) return fail(DLLM_ERR_SHAPE, "%s: L=%d outside [1, %d]", who, L, DLLM_MAX_L);
+    if (V < 1) return fail(DLLM_ERR_ARG, "%s: V < 1", who);
+    if (rows > DLLM_MAX_ROWS || (int64_t)rows * L > DLLM_MAX_POSITIONS)
+        return fail(DLLM_ERR_SHAPE, "%s: rows=%d, L=%d exceed the limits", who, rows, L);
+    int NV, NC;
+    size_t need;
+    shape_of(rows, L, V, dtype, NV, NC, need);
+    if ((int64_t)rows * L * NC >= (int64_t)1 << 31) return fail(DLLM_ERR_SHAPE, "%s: rows*L*chunks too large", who);
+    P.rows = rows; P.L = L; P.V = V; P.NV = NV; P.NC = NC;
+    P.partials = (float4 *)workspace;
+    return DLLM_OK;
+}
+
+// The workspace check, after every other argument check.
+dllm_status check_workspace(const char *who, dllm_dtype dtype, const void *workspace, size_t workspace_bytes,
+                            const StepParams &P) {
+    if (P.rows == 0) return DLLM_OK;
+    int NV, NC;
+    size_t need;
+    shape_of(P.rows, P.L, P.V, dtype, NV, NC, need);
+    if (!workspace) return fail(DLLM_ERR_ARG, "%s: null workspace", who);
+    if (workspace_bytes < need)
+        return fail(DLLM_ERR_ARG, "%s: workspace %zu bytes < %zu needed", who, workspace_bytes, need);
+    if (((uintptr_t)workspace & 15) != 0) return fail(DLLM_ERR_ARG, "%s: workspace not 16-byte aligned", who);
+    return DLLM_OK;
+}
+
+dllm_status check_score(const char *who, const void *logits, dllm_dtype dtype, int64_t pos_stride, int64_t row_stride,
+                        const uint8_t *mask_in, int32_t *status, StepParams &P) {
+    if (pos_stride < P.V || row_stride < (int64_t)P.L * pos_stride)
+        return fail(DLLM_ERR_ARG, "%s: strides too small (pos %lld, row %lld)", who, (long long)pos_stride,
+                    (long long)row_stride);
+    if (P.rows > 0 && (!logits || !mask_in || !status)) return fail(DLLM_ERR_ARG, "%s: null required pointer", who);
+    const int es = dtype == DLLM_BF16 ? 2 : 4;
+    P.logits = (const char *)logits;
+    P.pos_stride_b = pos_stride * es;
+    P.row_stride_b = row_stride * es;
+    P.mask_in = mask_in;
+    P.status = status;
+    return DLLM_OK;
+}
+
+dllm_status check_decide(const char *who, int32_t *input_ids, int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
+                         const float *threshold, const int32_t *p, const int32_t *b, float *conf, int32_t *argmax,
+                         uint8_t *done, int32_t *accept_len, int32_t *status, StepParams &P) {
+    if (W < P.L) return fail(DLLM_ERR_SHAPE, "%s: W=%d < L=%d", who, W, P.L);
+    if ((p == nullptr) != (b == nullptr)) return fail(DLLM_ERR_ARG, "%s: p and b must be both given or both NULL", who);
+    if (P.rows == 0) return DLLM_OK;
+    if (!input_ids || !mask_in || !mask_out || !threshold || !done || !accept_len || !status)
+        return fail(DLLM_ERR_ARG, "%s: null required pointer", who);
+    const int64_t S = (int64_t)P.rows * P.L;
+    if (mask_out != mask_in && (uintptr_t)mask_out < (uintptr_t)mask_in + (uintptr_t)S &&
+        (uintptr_t)mask_in < (uintptr_t)mask_out + (uintptr_t)S)
+        return fail(DLLM_ERR_ARG, "%s: mask_out partly overlaps mask_in", who);
+    P.W = W;
+    P.ids = input_ids; P.mask_in = mask_in; P.mask_out = mask_out; P.tau = threshold;
+    P.check_fit = p != nullptr;
+    P.p = p ? p : (const int32_t *)threshold;  // a readable array of `rows` 4-byte entries
+    P.b = b ? b : (const int32_t *)threshold;
+    P.conf_out = conf; P.arg_out = argmax; P.done = done; P.accept = accept_len;
+    P.status = status;
+    return DLLM_OK;
+}
+
+dllm_status launch_score(const StepParams &P, dllm_dtype dtype, hipStream_t st) {
+    const int es = dtype == DLLM_BF16 ? 2 : 4;
+    const int64_t S = (int64_t)P.rows * P.L;
+    const int NC = P.NC;
+    // vector path: 16-byte aligned rows whose length is a whole number of 16-byte vectors
+    const bool aligned = ((uintptr_t)P.logits & 15) == 0 && (P.pos_stride_b & 15) == 0 &&
+                         (P.row_stride_b & 15) == 0 && (P.V % (16 / es)) == 0;
+    // grid: one workgroup per compute unit; more when the LDS window of masked slots would
+    // exceed 2048 entries (24 KiB of dynamic LDS); fewer when a fully masked box has fewer chunks
+    // than that many waves
+    int64_t grid = cu_count();
+    if (grid < (S + 2047) / 2048) grid = (S + 2047) / 2048;
+    const int64_t most = (S * NC + kWaves - 1) / kWaves;
+    if (grid > most) grid = most;
+    if (grid < 1) grid = 1;
+    // window: masked slots touched by one workgroup's ceil(M*NC/grid) chunks, for M <= S
+    const int64_t per = (S * NC + grid - 1) / grid;
+    const int win = (int)((per + NC - 1) / NC + 2);
+    const size_t lds = (size_t)win * (sizeof(int64_t) + sizeof(int));
+    if (dtype == DLLM_BF16) {
+        if (aligned) hipLaunchKernelGGL((score_kernel<true, true>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
+        else hipLaunchKernelGGL((score_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
+    } else {
+        if (aligned) hipLaunchKernelGGL((score_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
+        else hipLaunchKernelGGL((score_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
+    }
+    return check_hip(hipGetLastError(), "dllm_step score launch");
+}
+
+dllm_status launch_decide(const StepParams &P, hipStream_t st) {
+    const size_t lds = (size_t)P.L * 9 + 16;
+    hipLaunchKernelGGL(decide_kernel, dim3((unsigned)P.rows), dim3(kDecideThreads), lds, st, P);
+    return check_hip(hipGetLastError(), "dllm_step decide launch");
+}
+
 }  // namespace
 
 extern "C" size_t dllm_step_workspace_bytes(int32_t rows, int32_t L, int32_t V, dllm_dtype dtype) {
@@ -559,71 +663,42 @@ extern "C" dllm_status dllm_step(void *stream, const void *logits, dllm_dtype dt
                                  const int32_t *p, const int32_t *b, float *conf, int32_t *argmax,
                                  uint8_t *done, int32_t *accept_len, void *workspace, size_t workspace_bytes,
                                  int32_t *status) {
-    if (dtype != DLLM_FP32 && dtype != DLLM_BF16) return fail(DLLM_ERR_DTYPE, "dllm_step: unknown dtype %d", (int)dtype);
-    if (rows < 0) return fail(DLLM_ERR_ARG, "dllm_step: rows < 0");
-    if (L < 1 || L > DLLM_MAX_L) return fail(DLLM_ERR_SHAPE, "dllm_step: L=%d outside [1, %d]", L, DLLM_MAX_L);
-    if (V < 1) return fail(DLLM_ERR_ARG, "dllm_step: V < 1");
-    if (W < L) return fail(DLLM_ERR_SHAPE, "dllm_step: W=%d < L=%d", W, L);
-    if (rows > DLLM_MAX_ROWS || (int64_t)rows * L > DLLM_MAX_POSITIONS)
-        return fail(DLLM_ERR_SHAPE, "dllm_step: rows=%d, L=%d exceed the limits", rows, L);
-    if (pos_stride < V || row_stride < (int64_t)L * pos_stride)
-        return fail(DLLM_ERR_ARG, "dllm_step: strides too small (pos %lld, row %lld)", (long long)pos_stride,
-                    (long long)row_stride);
-    if ((p == nullptr) != (b == nullptr)) return fail(DLLM_ERR_ARG, "dllm_step: p and b must be both given or both NULL");
-    if (rows == 0) return DLLM_OK;
-    if (!logits || !input_ids || !mask_in || !mask_out || !threshold || !done || !accept_len || !workspace || !status)
-        return fail(DLLM_ERR_ARG, "dllm_step: null required pointer");
-    const int64_t S = (int64_t)rows * L;
-    if (mask_out != mask_in && (uintptr_t)mask_out < (uintptr_t)mask_in + (uintptr_t)S &&
-        (uintptr_t)mask_in < (uintptr_t)mask_out + (uintptr_t)S)
-        return fail(DLLM_ERR_ARG, "dllm_step: mask_out partly overlaps mask_in");
-    int NV, NC;
-    size_t need;
-    shape_of(rows, L, V, dtype, NV, NC, need);
-    if (workspace_bytes < need)
-        return fail(DLLM_ERR_ARG, "dllm_step: workspace %zu bytes < %zu needed", workspace_bytes, need);
-    if (((uintptr_t)workspace & 15) != 0) return fail(DLLM_ERR_ARG, "dllm_step: workspace not 16-byte aligned");
-    if (S * NC >= (int64_t)1 << 31) return fail(DLLM_ERR_SHAPE, "dllm_step: rows*L*chunks too large");
-
-    const int es = dtype == DLLM_BF16 ? 2 : 4;
-    StepParams P;
-    P.logits = (const char *)logits;
-    P.pos_stride_b = pos_stride * es;
-    P.row_stride_b = row_stride * es;
-    P.rows = rows; P.L = L; P.V = V; P.NV = NV; P.NC = NC; P.W = W;
-    P.ids = input_ids; P.mask_in = mask_in; P.mask_out = mask_out; P.tau = threshold;
-    P.check_fit = p != nullptr;
-    P.p = p ? p : (const int32_t *)threshold;  // a readable array of `rows` 4-byte entries
-    P.b = b ? b : (const int32_t *)threshold;
-    P.conf_out = conf; P.arg_out = argmax; P.done = done; P.accept = accept_len;
-    P.partials = (float4 *)workspace;
-    P.status = status;
-
-    // vector path: 16-byte aligned rows whose length is a whole number of 16-byte vectors
-    const bool aligned = ((uintptr_t)logits & 15) == 0 && (P.pos_stride_b & 15) == 0 &&
-                         (P.row_stride_b & 15) == 0 && (V % (16 / es)) == 0;
-    // grid: one workgroup per compute unit; more when the LDS window of masked slots would
-    // exceed 2048 entries (24 KiB of dynamic LDS); fewer when a fully masked box has fewer chunks than that many waves
-    int64_t grid = cu_count();
-    if (grid < (S + 2047) / 2048) grid = (S + 2047) / 2048;
-    const int64_t most = (S * NC + kWaves - 1) / kWaves;
-    if (grid > most) grid = most;
-    if (grid < 1) grid = 1;
-    // window: masked slots touched by one workgroup's ceil(M*NC/grid) chunks, for M <= S
-    const int64_t per = (S * NC + grid - 1) / grid;
-    const int win = (int)((per + NC - 1) / NC + 2);
-    const size_t lds = (size_t)win * (sizeof(int64_t) + sizeof(int));
-    hipStream_t st = (hipStream_t)stream;
-    if (dtype == DLLM_BF16) {
-        if (aligned) hipLaunchKernelGGL((score_kernel<true, true>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
-        else hipLaunchKernelGGL((score_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
-    } else {
-        if (aligned) hipLaunchKernelGGL((score_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
-        else hipLaunchKernelGGL((score_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
-    }
-    dllm_status rc = check_hip(hipGetLastError(), "dllm_step score launch");
+    StepParams P{};
+    dllm_status rc = check_shape("dllm_step", dtype, rows, L, V, workspace, P);
+    if (rc == DLLM_OK) rc = check_score("dllm_step", logits, dtype, pos_stride, row_stride, mask_in, status, P);
+    if (rc == DLLM_OK)
+        rc = check_decide("dllm_step", input_ids, W, mask_in, mask_out, threshold, p, b, conf, argmax, done,
+                          accept_len, status, P);
+    if (rc == DLLM_OK) rc = check_workspace("dllm_step", dtype, workspace, workspace_bytes, P);
+    if (rc != DLLM_OK || rows == 0) return rc;
+    rc = launch_score(P, dtype, (hipStream_t)stream);
     if (rc != DLLM_OK) return rc;
-    const size_t lds2 = (size_t)L * 9 + 16;
-    hipLaunchKernelGGL(decide_kernel, dim3((unsigned)rows), dim3(kDecideThreads), lds2, st, P);
-    return check_hip(hipGetLastError(), "dllm_step decide launch");
+    return launch_decide(P, (hipStream_t)stream);
+}
+
+extern "C" dllm_status dllm_step_score(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+                                       int64_t row_stride, int32_t rows, int32_t L, int32_t V,
+                                       const uint8_t *mask_in, void *workspace, size_t workspace_bytes,
+                                       int32_t *status) {
+    StepParams P{};
+    dllm_status rc = check_shape("dllm_step_score", dtype, rows, L, V, workspace, P);
+    if (rc == DLLM_OK) rc = check_score("dllm_step_score", logits, dtype, pos_stride, row_stride, mask_in, status, P);
+    if (rc == DLLM_OK) rc = check_workspace("dllm_step_score", dtype, workspace, workspace_bytes, P);
+    if (rc != DLLM_OK || rows == 0) return rc;
+    return launch_score(P, dtype, (hipStream_t)stream);
+}
+
+extern "C" dllm_status dllm_step_decide(void *stream, dllm_dtype dtype, int32_t rows, int32_t L, int32_t V,
+                                        int32_t *input_ids, int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
+                                        const float *threshold, const int32_t *p, const int32_t *b, float *conf,
+                                        int32_t *argmax, uint8_t *done, int32_t *accept_len, void *workspace,
+                                        size_t workspace_bytes, int32_t *status) {
+    StepParams P{};
+    dllm_status rc = check_shape("dllm_step_decide", dtype, rows, L, V, workspace, P);
+    if (rc == DLLM_OK)
+        rc = check_decide("dllm_step_decide", input_ids, W, mask_in, mask_out, threshold, p, b, conf, argmax,
+                          done, accept_len, status, P);
+    if (rc == DLLM_OK) rc = check_workspace("dllm_step_decide", dtype, workspace, workspace_bytes, P);
+    if (rc != DLLM_OK || rows == 0) return rc;
+    return launch_decide(P, (hipStream_t)stream);
 }

@@ -128,8 +128,30 @@ dllm_status dllm_step(void *stream, const void *logits, dllm_dtype dtype, int64_
                       const int32_t *p, const int32_t *b, float *conf, int32_t *argmax, uint8_t *done,
                       int32_t *accept_len, void *workspace, size_t workspace_bytes, int32_t *status);
 
-/* Bytes of workspace dllm_step needs for this shape (0 for invalid arguments). */
+/* Bytes of workspace dllm_step (or the pair below) needs for this shape (0 for invalid
+ * arguments). */
 size_t dllm_step_workspace_bytes(int32_t rows, int32_t L, int32_t V, dllm_dtype dtype);
+
+/* dllm_step_score and dllm_step_decide — dllm_step in its two halves, for callers that time,
+ * overlap or schedule them apart.  Calling dllm_step_score, then dllm_step_decide on the same
+ * stream with the same dtype, rows, L, V, mask_in and workspace, equals one dllm_step call
+ * bit for bit.
+ *
+ * dllm_step_score: for every masked slot (mask_in != 0), reduces its logits row ([DiLaServe] §三
+ * 3.1: the confidence is a softmax probability; [FDFO] §工程设计一: only masked slots are
+ * predicted) to per-chunk partial results (max, sum of exp(x - max), first index at the max) in
+ * the workspace.  Arguments as for dllm_step; writes only the workspace (and *status).
+ * dllm_step_decide: merges those partials in a fixed order into conf and argmax and applies the
+ * LowConfidence rule, with the outputs and conditions of dllm_step.  It reads no logits.
+ * Errors: those of dllm_step that concern each half's own arguments. */
+dllm_status dllm_step_score(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+                            int64_t row_stride, int32_t rows, int32_t L, int32_t V, const uint8_t *mask_in,
+                            void *workspace, size_t workspace_bytes, int32_t *status);
+dllm_status dllm_step_decide(void *stream, dllm_dtype dtype, int32_t rows, int32_t L, int32_t V,
+                             int32_t *input_ids, int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
+                             const float *threshold, const int32_t *p, const int32_t *b, float *conf,
+                             int32_t *argmax, uint8_t *done, int32_t *accept_len, void *workspace,
+                             size_t workspace_bytes, int32_t *status);
 
 /* dllm_pack — materialise the left-padded bounding box for the active rows.
  *

@@ -79,6 +79,36 @@ def test_step_rejects_bad_arguments(kw, code):
     assert _lib.last_error() != ""
 
 
+def test_step_halves_reject_bad_arguments():
+    L = _lib.lib()
+    need = L.dllm_step_workspace_bytes(4, 32, 1024, 1)
+    f, ws = FAKE, ctypes.c_void_p(0x10000)
+
+    def score(**kw):
+        a = dict(logits=f, dtype=1, ps=1024, rs=32 * 1024, rows=4, L=32, V=1024, mask=f, ws=ws, n=need, status=f)
+        a.update(kw)
+        return L.dllm_step_score(None, a["logits"], a["dtype"], a["ps"], a["rs"], a["rows"], a["L"], a["V"],
+                                 a["mask"], a["ws"], a["n"], a["status"])
+
+    def decide(**kw):
+        a = dict(dtype=1, rows=4, L=32, V=1024, ids=f, W=40, mi=f, mo=ctypes.c_void_p(0x2000), tau=f, done=f,
+                 acc=f, ws=ws, n=need, status=f)
+        a.update(kw)
+        return L.dllm_step_decide(None, a["dtype"], a["rows"], a["L"], a["V"], a["ids"], a["W"], a["mi"], a["mo"],
+                                  a["tau"], None, None, None, None, a["done"], a["acc"], a["ws"], a["n"], a["status"])
+    assert score(dtype=5) == _lib.DLLM_ERR_DTYPE
+    assert score(logits=None) == _lib.DLLM_ERR_ARG
+    assert score(ps=100) == _lib.DLLM_ERR_ARG
+    assert score(n=need - 16) == _lib.DLLM_ERR_ARG
+    assert score(L=0) == _lib.DLLM_ERR_SHAPE
+    assert score(rows=0, logits=None, mask=None) == _lib.DLLM_OK
+    assert decide(W=31) == _lib.DLLM_ERR_SHAPE
+    assert decide(done=None) == _lib.DLLM_ERR_ARG
+    assert decide(ws=None) == _lib.DLLM_ERR_ARG
+    assert decide(mo=ctypes.c_void_p(0x1000 + 1)) == _lib.DLLM_ERR_ARG
+    assert decide(rows=0, ids=None) == _lib.DLLM_OK
+
+
 def test_step_rows_zero_is_noop():
     assert _step(rows=0, logits=None, ids=None) == _lib.DLLM_OK
 

@@ -184,6 +184,35 @@ def test_step_many_slots(rows, L, V, dtype, p_mask, moff):
     check_step(logits, dtype, ids, mask, tau, g)
 
 
+def test_step_halves_equal_step():
+    # dllm_step_score then dllm_step_decide gives dllm_step's outputs bit for bit
+    from confidence_block_unmasking_amd import api
+    w = configs.config3()
+    pk, logits = _packed_step_inputs(w)
+    a = gpu_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"])
+    rows, L, V = logits.shape
+    lg = _to_dev_logits(logits, w.dtype)
+    ids = torch.from_numpy(pk["box_ids"].astype(np.int32)).cuda()
+    mask = torch.from_numpy(pk["mask"].astype(np.uint8)).cuda()
+    mout = torch.empty_like(mask)
+    tau = torch.from_numpy(pk["threshold"].astype(np.float32)).cuda()
+    done = torch.empty(rows, dtype=torch.uint8, device="cuda")
+    acc = torch.empty(rows, dtype=torch.int32, device="cuda")
+    conf = torch.empty((rows, L), dtype=torch.float32, device="cuda")
+    arg = torch.empty((rows, L), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = api.new_workspace(rows, L, V, torch.bfloat16)
+    api.dllm_step_score(lg, mask, ws, status)
+    api.dllm_step_decide(torch.bfloat16, rows, L, V, ids, mask, mout, tau, done, acc, ws, status, conf=conf,
+                         argmax=arg)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    b = dict(ids=ids.cpu().numpy(), mask=mout.cpu().numpy(), done=done.cpu().numpy(), accept=acc.cpu().numpy(),
+             conf=conf.cpu().numpy(), argmax=arg.cpu().numpy())
+    for k in b:
+        assert np.array_equal(a[k], b[k]), k
+
+
 def test_step_in_place_mask_update():
     # mask_out = mask_in: the same results as with two buffers
     w = configs.config3()
