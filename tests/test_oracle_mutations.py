@@ -1,0 +1,74 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake (a flipped sign, an off-by-one index, a `>` turned into `>=`, a
+reordered rule) in a scratch copy of `oracle/`, then runs the pin tests of that file against the
+copy; they must fail.  A control run of the unmodified copy must pass.  Everything runs on the
+CPU in subprocesses; the repository's own oracle is never modified.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+STEP = "tests/test_oracle_step.py"
+PACK = "tests/test_oracle_pack_compact.py"
+LOOP = "tests/test_oracle_loop.py"
+
+MUTATIONS = [
+    ("oracle/step.py", "S = float(np.sum(np.exp(x - m)))", "S = float(np.sum(np.exp(m - x)))", STEP),
+    ("oracle/step.py", "a = int(np.flatnonzero(x == m)[0])", "a = int(np.flatnonzero(x == m)[-1])", STEP),
+    ("oracle/step.py", "np.asarray(conf, np.float64) > t", "np.asarray(conf, np.float64) >= t", STEP),
+    ("oracle/step.py", "if masked[j] and conf[j] > best_c", "if masked[j] and conf[j] >= best_c", STEP),
+    ("oracle/step.py", "ids[r, W - L + j] = arg[r, j]", "ids[r, W - L + j - 1] = arg[r, j]", STEP),
+    ("oracle/step.py", "accept[r] = L if done[r] else 0", "accept[r] = 1 if done[r] else 0", STEP),
+    ("oracle/pack.py", "return int(p) + (int(b) + 1) * int(L)", "return int(p) + int(b) * int(L)", PACK),
+    ("oracle/pack.py", "box_pos[r, pad:] = np.arange(w)", "box_pos[r, pad:] = np.arange(1, w + 1)", PACK),
+    ("oracle/compact.py", "and queue_p[i] + L <= W_A:", "and queue_p[i] + L < W_A:", PACK),
+    ("oracle/compact.py", "if best is None or queue_p[i] > queue_p[best]:",
+     "if best is None or queue_p[i] >= queue_p[best]:", PACK),
+    ("oracle/compact.py", "if budget > 0 and (n_active + 1) * new_W > budget:",
+     "if budget > 0 and n_active * new_W > budget:", PACK),
+    ("oracle/compact.py", "if b[q] >= K[q] or hit_eos:", "if b[q] > K[q] or hit_eos:", PACK),
+    ("oracle/compact.py", "movers = sorted([r for r in occupied if r >= n_new], reverse=True)",
+     "movers = sorted([r for r in occupied if r >= n_new])", PACK),
+    ("oracle/compact.py", "slots = sorted(freed) + list(range(rows, rows_cap))",
+     "slots = list(range(rows, rows_cap)) + sorted(freed)", PACK),
+    ("oracle/loop.py", 'if mode == "sync" and out["done"].all():', 'if mode == "sync" and out["done"].any():', LOOP),
+]
+
+
+def _copy_tree(dst):
+    for d in ("oracle", "workload", "tests"):
+        shutil.copytree(os.path.join(ROOT, d), os.path.join(dst, d),
+                        ignore=shutil.ignore_patterns("__pycache__", "golden_tmp*"))
+    shutil.copy(os.path.join(ROOT, "pytest.ini"), dst)
+
+
+def _run_pins(dst, pin_file):
+    env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
+    return subprocess.run([sys.executable, "-m", "pytest", pin_file, "-x", "-q", "-m", "not gpu",
+                           "-p", "no:cacheprovider"], cwd=dst, env=env, capture_output=True, text=True,
+                          timeout=300)
+
+
+def test_unmodified_copy_passes(tmp_path):
+    _copy_tree(str(tmp_path))
+    for pin in (STEP, PACK, LOOP):
+        r = _run_pins(str(tmp_path), pin)
+        assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+
+
+@pytest.mark.parametrize("path,old,new,pin", MUTATIONS, ids=[f"{m[0]}:{i}" for i, m in enumerate(MUTATIONS)])
+def test_planted_mistake_is_caught(tmp_path, path, old, new, pin):
+    _copy_tree(str(tmp_path))
+    f = os.path.join(str(tmp_path), path)
+    src = open(f).read()
+    assert src.count(old) == 1, f"mutation site not found once in {path}: {old}"
+    with open(f, "w") as fh:
+        fh.write(src.replace(old, new))
+    r = _run_pins(str(tmp_path), pin)
+    assert r.returncode != 0, f"planted mistake survived the pins of {pin}: {path}: {old} -> {new}"
