@@ -9,10 +9,15 @@
 //   end of sequence; §II-D — queue sorted by prompt length, refill with a candidate whose p + L
 //   fits the current box ("sand filling"), Cost of Eq.(1); §II-E — each block starts fully masked.
 //
-// One workgroup of 1024 threads: the O(rows * L) scatter, commits and fills run in parallel; the
-// greedy admission is inherently sequential (each choice changes the box width) and runs on one
-// thread over LDS copies of the queue's prompt lengths, with a binary search for the best fit.
-// The queue is compacted in place (in order) with a parallel prefix scan.
+// One workgroup of 1024 threads.  The kernel is latency-bound (kilobytes of data, a chain of
+// dependent reads), so it is laid out to pay few memory round trips: the request fields of every
+// row and every queue entry are loaded once, up front (the queue ids speculatively up to the queue
+// capacity, so they need not wait for the queue length), and all later phases work from registers
+// and LDS.  The scatter of the finished step, the commit and the fresh-block fill are one pass that
+// writes every arena and mask element once.  The greedy admission is inherently sequential (each
+// choice changes the box width) and runs on one thread over LDS copies of the queue's prompt
+// lengths, with a binary search for the best fit.  The queue is compacted in place (in order) with a
+// parallel prefix scan.
 #include "common.h"
 
 namespace {
@@ -37,132 +42,174 @@ struct CompactParams {
     int32_t *status;
 };
 
-__device__ __forceinline__ int64_t block_start(const dllm_reqs &R, int q, int blk, int L) {
-    return R.arena_off[q] + (int64_t)R.p[q] + (int64_t)blk * L;
-}
+constexpr int kRowsPerThread = DLLM_MAX_ROWS / kThreads;   // rows owned by one thread (registers)
+constexpr int kQPerThread = DLLM_MAX_QUEUE / kThreads;      // queue entries loaded by one thread
 
-__device__ int block_reduce_max(int v, int *scratch) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_max_i(v);
-    __syncthreads();
-    if (lane == 0) scratch[wave] = v;
-    __syncthreads();
-    int r = scratch[0];
-    for (int w = 1; w < kWaves; ++w) r = max(r, scratch[w]);
-    return r;
-}
-__device__ int block_reduce_sum(int v, int *scratch) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_sum_i(v);
-    __syncthreads();
-    if (lane == 0) scratch[wave] = v;
-    __syncthreads();
-    int r = 0;
-    for (int w = 0; w < kWaves; ++w) r += scratch[w];
-    return r;
-}
+// Row actions decided in phase 2 (s_act).
+constexpr uint8_t kKeep = 0;      // unfinished block: scatter it back, keep the row
+constexpr uint8_t kAdvance = 1;   // finished, blocks left: commit, then a fresh masked block
+constexpr uint8_t kEvict = 2;     // finished, last block (or end of sequence): commit, free the row
+constexpr uint8_t kNone = 3;      // no (valid) request in this row
 
 __global__ __launch_bounds__(kThreads) void compact_kernel(CompactParams P) {
-    extern __shared__ int32_t lds[];
-    __shared__ int red[kWaves];
-    __shared__ int sh_nadm, sh_nnew, sh_qlen, sh_bad, sh_badid;
+    extern __shared__ int64_t lds64[];
+    __shared__ int red3[kWaves][3];
+    __shared__ int sh_qlen, sh_bad, sh_badid;
     const int tid = threadIdx.x;
-    const int rows = P.rows, L = P.L, cap = P.rows_cap;
+    const int rows = P.rows, L = P.L, cap = P.rows_cap, qcap = P.q_cap;
     const dllm_reqs &R = P.R;
-    int32_t *s_row = lds;                        // [cap]   row -> request (-1 free)
-    int32_t *s_adm = s_row + cap;                // [cap]   admitted queue indices, in order
-    int32_t *s_qp = s_adm + cap;                 // [q_cap] prompt length of queue entries
-    int32_t *s_qid = s_qp + P.q_cap;             // [q_cap] queue ids
-    uint8_t *s_flag = (uint8_t *)(s_qid + P.q_cap);   // [cap] 1 = fresh block needed
-    uint8_t *s_taken = s_flag + cap;             // [q_cap]
+    int64_t *s_old = lds64;                      // [cap]   arena start of the row's current block
+    int32_t *s_row = (int32_t *)(s_old + cap);   // [cap]   row -> request (-1 free); the new layout
+    int32_t *s_q0 = s_row + cap;                 // [cap]   row -> request on entry (read by the scatter
+                                                 //         while wave 0 rewrites s_row)
+    int32_t *s_adm = s_q0 + cap;                 // [cap]   admitted queue indices, in order
+    int32_t *s_qp = s_adm + cap;                 // [qcap]  prompt length of queue entries
+    int32_t *s_qid = s_qp + qcap;                // [qcap]  queue ids
+    uint8_t *s_act = (uint8_t *)(s_qid + qcap);  // [cap]   row action
+    uint8_t *s_taken = s_act + cap;              // [qcap]
 
+    // 1. every load that does not depend on another one: queue length, the rows' request ids and
+    //    done flags, the queue ids (up to its capacity); then the request fields they point to
+    int qlen_raw = 0;
+    if (tid == 0) qlen_raw = *P.q_len;
+    int rq[kRowsPerThread], rdone[kRowsPerThread];
+#pragma unroll
+    for (int k = 0; k < kRowsPerThread; ++k) {
+        const int r = tid + k * kThreads;
+        rq[k] = r < rows ? P.row_req[r] : -1;
+        rdone[k] = (r < rows && P.box_ids) ? P.done[r] : 0;
+    }
+    int qi[kQPerThread];
+#pragma unroll
+    for (int k = 0; k < kQPerThread; ++k) {
+        const int i = tid + k * kThreads;
+        qi[k] = i < qcap ? P.q_ids[i] : -1;
+    }
+    int rp[kRowsPerThread], rb[kRowsPerThread], rK[kRowsPerThread], rst[kRowsPerThread];
+    int64_t roff[kRowsPerThread];
+#pragma unroll
+    for (int k = 0; k < kRowsPerThread; ++k) {
+        const int q = rq[k];
+        const bool in = q >= 0 && q < R.n_req;
+        rp[k] = in ? R.p[q] : 0;
+        rb[k] = in ? R.b[q] : 0;
+        rK[k] = in ? R.K[q] : 0;
+        rst[k] = in ? R.state[q] : -1;
+        roff[k] = in ? R.arena_off[q] : 0;
+    }
+    int qp[kQPerThread];
+    bool qok[kQPerThread];
+#pragma unroll
+    for (int k = 0; k < kQPerThread; ++k) {
+        const int id = qi[k];
+        const bool in = id >= 0 && id < R.n_req;
+        qp[k] = in ? R.p[id] : 0;
+        qok[k] = in && R.state[id] == 0 && R.K[id] >= 1;
+    }
     if (tid == 0) {
-        int ql = *P.q_len;
-        sh_bad = (ql < 0 || ql > P.q_cap);
-        sh_qlen = sh_bad ? 0 : ql;
+        sh_bad = (qlen_raw < 0 || qlen_raw > qcap);
+        sh_qlen = sh_bad ? 0 : qlen_raw;
         sh_badid = 0;
         if (sh_bad) set_status(P.status, DLLM_ERR_CAPACITY);
     }
-    for (int r = tid; r < cap; r += kThreads) {
-        int q = -1;
-        if (r < rows) {
-            q = P.row_req[r];
-            if (q < 0 || q >= R.n_req || R.state[q] != 1 || R.b[q] < 0 || R.b[q] >= R.K[q]) {
-                set_status(P.status, DLLM_ERR_ARG);
-                q = -1;
-            }
-        }
-        s_row[r] = q;
-        s_flag[r] = 0;
-    }
     __syncthreads();
-    for (int i = tid; i < sh_qlen; i += kThreads) {
-        const int id = P.q_ids[i];
-        const bool ok = id >= 0 && id < R.n_req && R.state[id] == 0 && R.K[id] >= 1;
-        s_qid[i] = id;
-        s_qp[i] = ok ? R.p[id] : 0;
-        s_taken[i] = 0;
-        if (!ok) sh_badid = 1;
-    }
-    __syncthreads();
-    if (sh_badid && tid == 0) set_status(P.status, DLLM_ERR_ARG);
-    // a queue holding an invalid or non-queued id is left untouched and admits nothing
-    const int qlen = sh_badid ? 0 : sh_qlen;
-    const bool touch_queue = !sh_bad && !sh_badid;
+    const int qlen0 = sh_qlen;
 
-    int n_evicted = 0;
-    if (P.box_ids) {
-        // 1. scatter active blocks (the last L box columns) and masks back to their requests
-        for (int idx = tid; idx < rows * L; idx += kThreads) {
-            const int r = idx / L, j = idx - (idx / L) * L;
-            const int q = s_row[r];
-            if (q < 0) continue;
-            R.arena[block_start(R, q, R.b[q], L) + j] = P.box_ids[(int64_t)r * P.W + (P.W - L) + j];
-            R.blk_mask[(int64_t)q * L + j] = P.mask[(int64_t)r * L + j];
+    // 2. validate; per row: its action and its blocks' arena starts
+    int ev = 0, wloc = 0, nloc = 0;
+#pragma unroll
+    for (int k = 0; k < kRowsPerThread; ++k) {
+        const int r = tid + k * kThreads;
+        if (r >= cap) continue;
+        int q = rq[k];
+        if (r < rows && (q < 0 || q >= R.n_req || rst[k] != 1 || rb[k] < 0 || rb[k] >= rK[k])) {
+            set_status(P.status, DLLM_ERR_ARG);
+            q = -1;
         }
-        __syncthreads();
-        // 2. commit finished blocks: advance; evict, or open a fresh block in the same row
-        int ev = 0;
-        for (int r = tid; r < rows; r += kThreads) {
-            const int q = s_row[r];
-            if (q < 0 || !P.done[r]) continue;
+        uint8_t act = q < 0 ? kNone : kKeep;
+        int b = rb[k];
+        if (q >= 0 && P.box_ids && rdone[k]) {
             bool eos = false;
             if (P.eos_id >= 0)
                 for (int j = 0; j < L; ++j) eos |= P.box_ids[(int64_t)r * P.W + (P.W - L) + j] == P.eos_id;
-            const int nb = R.b[q] + 1;
-            R.b[q] = nb;
-            if (nb >= R.K[q] || eos) {
+            act = (b + 1 >= rK[k] || eos) ? kEvict : kAdvance;
+            R.b[q] = b + 1;
+            if (act == kEvict) {
                 R.state[q] = 2;
-                s_row[r] = -1;
                 ++ev;
             } else {
-                s_flag[r] = 1;
+                ++b;
             }
         }
-        n_evicted = block_reduce_sum(ev, red);     // includes a barrier
-        for (int idx = tid; idx < rows * L; idx += kThreads) {
-            const int r = idx / L, j = idx - (idx / L) * L;
-            if (!s_flag[r]) continue;
-            const int q = s_row[r];
-            R.arena[block_start(R, q, R.b[q], L) + j] = P.mask_id;
-            R.blk_mask[(int64_t)q * L + j] = 1;
-        }
-    }
-    __syncthreads();
-
-    // 3. admission (sequential, one thread): current width and survivor count first
-    int wloc = 0, nloc = 0;
-    for (int r = tid; r < rows; r += kThreads) {
-        const int q = s_row[r];
-        if (q >= 0) {
-            wloc = max(wloc, R.p[q] + (R.b[q] + 1) * L);
+        s_old[r] = roff[k] + rp[k] + (int64_t)rb[k] * L;
+        s_q0[r] = q;
+        s_act[r] = act;
+        s_row[r] = (act == kNone || act == kEvict) ? -1 : q;
+        if (act == kKeep || act == kAdvance) {
+            wloc = max(wloc, rp[k] + (b + 1) * L);
             ++nloc;
         }
     }
-    const int W_A0 = block_reduce_max(wloc, red);
-    const int n_act0 = block_reduce_sum(nloc, red);
-    if (tid == 0) {
-        int n_act = n_act0, W_A = W_A0, n_adm = 0, lo = 0;
+#pragma unroll
+    for (int k = 0; k < kQPerThread; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < qlen0) {
+            s_qid[i] = qi[k];
+            s_qp[i] = qok[k] ? qp[k] : 0;
+            s_taken[i] = 0;
+            if (!qok[k]) sh_badid = 1;
+        }
+    }
+    {   // this wave's part of the counts wave 0 needs; one barrier publishes them with phase 2
+        const int e = wave_sum_i(ev), wm = wave_max_i(wloc), n = wave_sum_i(nloc);
+        if ((tid & 63) == 0) { red3[tid >> 6][0] = e; red3[tid >> 6][1] = wm; red3[tid >> 6][2] = n; }
+    }
+    __syncthreads();
+    // a queue holding an invalid or non-queued id is left untouched and admits nothing
+    const int qlen = sh_badid ? 0 : qlen0;
+    const bool touch_queue = !sh_bad && !sh_badid;
+    const int wave = tid >> 6, lane = tid & 63;
+
+    // 3. waves 1..: the step's block back to its request, in one pass: the finished block (or the
+    //    unfinished one with its mask) goes to the arena; an advancing request's next block opens
+    //    fully masked.  Then these waves are done.
+    if (wave != 0) {
+        if (P.box_ids) {
+            for (int idx = tid - 64; idx < rows * L; idx += kThreads - 64) {
+                const int r = idx / L, j = idx - (idx / L) * L;
+                const uint8_t act = s_act[r];
+                if (act == kNone) continue;
+                const int q = s_q0[r];
+                const int32_t tok = P.box_ids[(int64_t)r * P.W + (P.W - L) + j];
+                const uint8_t m = P.mask[(int64_t)r * L + j];
+                const int64_t old = s_old[r];
+                R.arena[old + j] = tok;
+                if (act == kAdvance) {
+                    R.arena[old + L + j] = P.mask_id;
+                    R.blk_mask[(int64_t)q * L + j] = 1;
+                } else {
+                    // kept, or evicted (its last block committed, its all-zero mask stored as well)
+                    R.blk_mask[(int64_t)q * L + j] = m;
+                }
+            }
+        }
+        return;
+    }
+
+    // 4.. wave 0 alone from here: every step below is wave-synchronous (no workgroup barrier).  LDS
+    //    accesses of one wave take effect in program order, so lanes see each other's writes.
+    int n_evicted = 0, W_A0 = 0, n_act0 = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        n_evicted += red3[w][0];
+        W_A0 = max(W_A0, red3[w][1]);
+        n_act0 += red3[w][2];
+    }
+    if (sh_badid && lane == 0) set_status(P.status, DLLM_ERR_ARG);
+
+    // 4. admission (sequential, lane 0)
+    int n_adm = 0, n_new = n_act0, W_new = W_A0;
+    if (lane == 0) {
+        int n_act = n_act0, W_A = W_A0, lo = 0;
         while (n_act < cap) {
             while (lo < qlen && s_taken[lo]) ++lo;
             if (lo >= qlen) break;
@@ -195,78 +242,85 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactParams P) {
             ++n_act;
             W_A = newW;
         }
-        // 4. rows: freed rows ascending, then rows after the old end (every free row below `rows`
-        //    was freed by this call); then fill holes from the tail
-        int k = 0;
-        for (int r = 0; r < cap && k < n_adm; ++r)
-            if (s_row[r] < 0) s_row[r] = s_qid[s_adm[k++]];
-        const int n_new = n_act;
-        int h = 0, t = cap - 1;
-        while (true) {
-            while (h < n_new && s_row[h] >= 0) ++h;
-            while (t >= n_new && s_row[t] < 0) --t;
-            if (h >= n_new || t < n_new) break;
-            s_row[h] = s_row[t];
-            s_row[t] = -1;
-            ++h;
-            --t;
-        }
-        sh_nadm = n_adm;
-        sh_nnew = n_new;
+        n_new = n_act;
+        W_new = W_A;                               // widest row of the new active set
     }
-    __syncthreads();
-    const int n_adm = sh_nadm;
-    const int n_new = sh_nnew;
+    n_adm = __builtin_amdgcn_readfirstlane(n_adm);
+    n_new = __builtin_amdgcn_readfirstlane(n_new);
+    W_new = __builtin_amdgcn_readfirstlane(W_new);
 
-    // 5. write the layout; open block 0 of admitted requests
-    for (int r = tid; r < cap; r += kThreads) P.row_req[r] = s_row[r];
-    for (int idx = tid; idx < n_adm * L; idx += kThreads) {
+    // 5. open block 0 of admitted requests
+    for (int idx = lane; idx < n_adm * L; idx += 64) {
         const int a = idx / L, j = idx - (idx / L) * L;
-        const int q = s_qid[s_adm[a]];
+        const int ai = s_adm[a];
+        const int q = s_qid[ai];
         if (j == 0) {
             R.state[q] = 1;
             R.b[q] = 0;
         }
-        R.arena[block_start(R, q, 0, L) + j] = P.mask_id;
+        R.arena[R.arena_off[q] + s_qp[ai] + j] = P.mask_id;
         R.blk_mask[(int64_t)q * L + j] = 1;
     }
-    // 6. compact the queue in place, keeping order
-    int keep_prefix = 0;
+
+    // 6. rows.  Lane l looks after rows l*per .. l*per + per - 1.
+    //    (a) the k-th admitted request takes the k-th free row in ascending order: freed rows
+    //    first, then rows past the old end (every free row below `rows` was freed by this call);
+    //    (b) the rows left free below n_new (holes, ascending) take the requests of the occupied
+    //    rows at or above n_new (movers, descending); survivors otherwise stay where they are.
     {
-        const int per = (qlen + kThreads - 1) / kThreads;
-        const int i0 = min(qlen, tid * per), i1 = min(qlen, i0 + per);
+        const int per = (cap + 63) / 64;
+        const int r0 = min(cap, lane * per), r1 = min(cap, r0 + per);
+        int nf = 0;
+        for (int r = r0; r < r1; ++r) nf += s_row[r] < 0;
+        int ef = wave_incl_scan(nf) - nf;
+        for (int r = r0; r < r1; ++r) {
+            if (s_row[r] < 0) {
+                if (ef < n_adm) s_row[r] = s_qid[s_adm[ef]];
+                ++ef;
+            }
+        }
+        int nh = 0, nm = 0;
+        for (int r = r0; r < r1; ++r) {
+            const bool occ = s_row[r] >= 0;
+            nh += (r < n_new && !occ);
+            nm += (r >= n_new && occ);
+        }
+        int eh = wave_incl_scan(nh) - nh;
+        const int im = wave_incl_scan(nm);
+        const int tm = __builtin_amdgcn_readlane(im, 63);
+        int em = im - nm;
+        int *s_mv = s_adm;                         // the admitted list is placed: movers by rank
+        for (int r = r0; r < r1; ++r)
+            if (r >= n_new && s_row[r] >= 0) s_mv[tm - 1 - em++] = r;   // descending rank
+        for (int r = r0; r < r1; ++r)
+            if (r < n_new && s_row[r] < 0) s_row[r] = s_row[s_mv[eh++]];   // holes < n_new <= movers
+        for (int r = r0; r < r1; ++r)
+            if (r >= n_new && s_row[r] >= 0) s_row[r] = -1;
+        for (int r = r0; r < r1; ++r) P.row_req[r] = s_row[r];
+    }
+
+    // 7. compact the queue in place, keeping order (lane l: entries l*per .. l*per + per - 1)
+    {
+        const int per = (qlen + 63) / 64;
+        const int i0 = min(qlen, lane * per), i1 = min(qlen, i0 + per);
         int loc = 0;
         for (int i = i0; i < i1; ++i) loc += !s_taken[i];
-        const int lane = tid & 63, wave = tid >> 6;
-        const int incl = wave_incl_scan(loc);
-        __syncthreads();
-        if (lane == 63) red[wave] = incl;
-        __syncthreads();
-        int off = 0;
-        for (int w = 0; w < wave; ++w) off += red[w];
-        keep_prefix = off + incl - loc;
+        int keep = wave_incl_scan(loc) - loc;
         if (touch_queue)
             for (int i = i0; i < i1; ++i)
-                if (!s_taken[i]) P.q_ids[keep_prefix++] = s_qid[i];
+                if (!s_taken[i]) P.q_ids[keep++] = s_qid[i];
     }
-    __syncthreads();
-    // 7. meta (b of every active request is final now)
-    int wl = 0;
-    for (int r = tid; r < n_new; r += kThreads) {
-        const int q = s_row[r];
-        wl = max(wl, R.p[q] + (R.b[q] + 1) * L);
-    }
-    const int W_new = block_reduce_max(wl, red);
-    if (tid == 0) {
+    // 8. meta
+    if (lane == 0) {
         if (touch_queue) *P.q_len = qlen - n_adm;
         dllm_meta m;
         m.rows = n_new;
-        m.W = W_new;
+        m.W = n_new > 0 ? W_new : 0;
         m.n_evicted = n_evicted;
         m.n_admitted = n_adm;
         m.n_queued = touch_queue ? qlen - n_adm : sh_qlen;
         m.reserved = 0;
-        m.cost = (int64_t)n_new * W_new;
+        m.cost = (int64_t)n_new * m.W;
         *P.meta = m;
     }
 }
@@ -300,7 +354,7 @@ extern "C" dllm_status dllm_compact(void *stream, int32_t rows, int32_t L, int32
     P.mask = mask; P.done = done; P.row_req = row_req; P.R = *reqs;
     P.q_ids = queue->ids; P.q_len = queue->len; P.q_cap = queue->cap;
     P.budget = budget; P.meta = meta; P.status = status;
-    const size_t lds = (size_t)rows_cap * 8 + (size_t)queue->cap * 8 + (size_t)rows_cap + (size_t)queue->cap + 16;
+    const size_t lds = (size_t)rows_cap * 21 + (size_t)queue->cap * 9 + 16;
     int dev = 0, max_lds = 65536;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)

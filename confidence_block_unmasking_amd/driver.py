@@ -65,11 +65,11 @@ class Session:
         self.step_events = []          # (start, end) cuda events of each dllm_step, when timing
 
     @classmethod
-    def from_workload(cls, w, device="cuda", logits=None):
+    def from_workload(cls, w, device="cuda", logits=None, eos_id=-1):
         dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         return cls(w.p, w.K, w.b, w.state, w.threshold, w.arena_off, w.arena, w.blk_mask, w.row_req, w.rows,
                    w.queue, L=w.L, V=w.V, dtype=dt, rows_cap=w.rows_cap, budget=w.budget, mask_id=w.mask_id,
-                   pad_id=w.pad_id, device=device, logits=logits)
+                   pad_id=w.pad_id, eos_id=eos_id, device=device, logits=logits)
 
     # ---- views of the current box -------------------------------------------------------------
     def box(self):

@@ -58,15 +58,15 @@ def gpu_forward(w):
     return fwd
 
 
-def lockstep_run(w, full_score_max=64, sample=16, whole_rows=1, deep_every=1, seed=0, label=""):
+def lockstep_run(w, full_score_max=64, sample=16, whole_rows=1, deep_every=1, seed=0, label="", eos_id=-1):
     from confidence_block_unmasking_amd.driver import Session
     rng = np.random.default_rng(seed)
-    sess = Session.from_workload(w)
+    sess = Session.from_workload(w, eos_id=eos_id)
     st = _oracle_state(w)
     L, V = w.L, w.V
     fwd = gpu_forward(w)
     mg = sess.compact(with_box=False)
-    mo = ocompact.compact(st, w.rows, L, 0, w.mask_id, -1, w.budget, w.rows_cap)
+    mo = ocompact.compact(st, w.rows, L, 0, w.mask_id, eos_id, w.budget, w.rows_cap)
     _compare_meta(mg, mo)
     _compare_tables(sess, st)
     n_steps = n_scored = n_checked = n_amb = n_compacts = 0
@@ -144,7 +144,7 @@ def lockstep_run(w, full_score_max=64, sample=16, whole_rows=1, deep_every=1, se
             if w.mode == "sync" and done_o.all():
                 break
         mg = sess.compact(with_box=True)
-        mo = ocompact.compact(st, rows, L, W, w.mask_id, -1, w.budget, w.rows_cap, box_ids=ids_o, mask=mask_o,
+        mo = ocompact.compact(st, rows, L, W, w.mask_id, eos_id, w.budget, w.rows_cap, box_ids=ids_o, mask=mask_o,
                               done=done_o)
         n_compacts += 1
         _compare_meta(mg, mo)
@@ -156,7 +156,8 @@ def lockstep_run(w, full_score_max=64, sample=16, whole_rows=1, deep_every=1, se
     assert np.all(st["state"] == configs.FINISHED)
     print(f"{label}: steps={n_steps} scored={n_scored} checked={n_checked} ambiguous_rows={n_amb} "
           f"max_conf_err={max_err:.3g}", flush=True)
-    return dict(steps=n_steps, scored=n_scored, amb=n_amb, arena=st["arena"].copy(), stats=sess.stats)
+    return dict(steps=n_steps, scored=n_scored, amb=n_amb, arena=st["arena"].copy(), stats=sess.stats,
+                early=int(((st["state"] == configs.FINISHED) & (st["b"] < st["K"])).sum()))
 
 
 def test_pack_compact_parity_random_small():
@@ -167,6 +168,14 @@ def test_pack_compact_parity_random_small():
         w.row_req = np.full(cap, -1, np.int32)
         print(f"small run seed={seed} budget={budget} cap={cap}", flush=True)
         lockstep_run(w, full_score_max=10**9, label=f"small{seed}")
+
+
+def test_loop_end_of_sequence_evicts_early():
+    """With an end-of-sequence id, requests whose committed block holds it leave before block K."""
+    w = configs.small(L=4, V=16, n_act=0, n_q=10, K=4, seed=32, dtype="fp32", rows_cap=4, p_range=(1, 8))
+    w.row_req = np.full(4, -1, np.int32)
+    res = lockstep_run(w, full_score_max=10**9, label="eos", eos_id=7)
+    assert res["early"] >= 1
 
 
 def test_loop_schedule_invariance_gpu_vs_oracle_loop():
