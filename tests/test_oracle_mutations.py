@@ -17,6 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 STEP = "tests/test_oracle_step.py"
 PACK = "tests/test_oracle_pack_compact.py"
 LOOP = "tests/test_oracle_loop.py"
+QUOTA = "tests/test_oracle_quota.py"
 
 MUTATIONS = [
     ("oracle/step.py", "S = float(np.sum(np.exp(x - m)))", "S = float(np.sum(np.exp(m - x)))", STEP),
@@ -38,6 +39,11 @@ MUTATIONS = [
     ("oracle/compact.py", "slots = sorted(freed) + list(range(rows, rows_cap))",
      "slots = list(range(rows, rows_cap)) + sorted(freed)", PACK),
     ("oracle/loop.py", 'if mode == "sync" and out["done"].all():', 'if mode == "sync" and out["done"].any():', LOOP),
+    ("oracle/quota.py", "return [base + (1 if t < rem else 0) for t in range(S)]",
+     "return [base + (1 if t >= S - rem else 0) for t in range(S)]", QUOTA),
+    ("oracle/quota.py", "js.sort(key=lambda j: (-float(conf[j]), j))", "js.sort(key=lambda j: (-float(conf[j]), -j))",
+     QUOTA),
+    ("oracle/quota.py", "while t < S and pre + ks[t] <= u:", "while t < S and pre + ks[t] < u:", QUOTA),
 ]
 
 
@@ -57,7 +63,7 @@ def _run_pins(dst, pin_file):
 
 def test_unmodified_copy_passes(tmp_path):
     _copy_tree(str(tmp_path))
-    for pin in (STEP, PACK, LOOP):
+    for pin in (STEP, PACK, LOOP, QUOTA):
         r = _run_pins(str(tmp_path), pin)
         assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
 
