@@ -228,9 +228,16 @@ def run_gpu(args):
     ws, wsn = P(sess.workspace), sess.workspace.numel()
     score_args = [(stream, P(bufs[k]), _lib.DLLM_BF16, V, L * V, rows, L, V, P(mask_a), ws, wsn, P(sess.status))
                   for k in range(args.rotate)]
-    decide_args = (stream, _lib.DLLM_BF16, rows, L, V, P(box), W, P(mask_a), P(mask_b), P(sess.tau), P(sess.p_rows),
-                   P(sess.b_rows), P(sess.conf), P(sess.argmax), P(sess.done), P(sess.accept), ws, wsn,
-                   P(sess.status))
+    if args.rule == "quota":
+        decide_fn = lib.dllm_step_decide_quota
+        decide_args = (stream, _lib.DLLM_BF16, rows, L, V, P(box), W, P(mask_a), P(mask_b), args.steps_per_block,
+                       P(sess.p_rows), P(sess.b_rows), P(sess.conf), P(sess.argmax), P(sess.done), P(sess.accept), ws,
+                       wsn, P(sess.status))
+    else:
+        decide_fn = lib.dllm_step_decide
+        decide_args = (stream, _lib.DLLM_BF16, rows, L, V, P(box), W, P(mask_a), P(mask_b), P(sess.tau),
+                       P(sess.p_rows), P(sess.b_rows), P(sess.conf), P(sess.argmax), P(sess.done), P(sess.accept), ws,
+                       wsn, P(sess.status))
     pack_args, comp_args = [], []
     for c in copies:
         pack_args.append((stream, rows, L, W, w.pad_id, P(c.row_req), ctypes.byref(c.reqs), P(box),
@@ -253,7 +260,7 @@ def run_gpu(args):
         rc |= lib.dllm_step_score(*score_args[k % args.rotate])
         if e:
             e[1].record()
-        rc |= lib.dllm_step_decide(*decide_args)
+        rc |= decide_fn(*decide_args)
         rc |= lib.dllm_compact(*comp_args[k])
         return rc
 
@@ -292,6 +299,7 @@ def run_gpu(args):
         "config": {"workload": "Dream-shaped dynamic-threshold step: 64 requests, L=32, V=152064 bf16 logits, "
                                "thresholds {0.5..0.9}, masked fraction U[0.1,1.0]; step = pack + score + decide + "
                                "compact",
+                   "rule": "threshold" if args.rule == "threshold" else f"quota, {args.steps_per_block} steps per block",
                    "requests": w.rows, "block_len": L, "vocab": V, "logits_dtype": "bf16",
                    "masked_positions_per_step": M, "box_width": W, "logits_buffers": args.rotate},
         "logits_GBps": step_bytes * args.steps / elapsed / 1e9,
@@ -310,6 +318,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotate", type=int, default=4, help="logits buffers cycled through")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU work of the oracle baseline, in all")
+    ap.add_argument("--rule", choices=("threshold", "quota"), default="threshold",
+                    help="unmasking rule: LowConfidence threshold (default) or the fixed per-step quota")
+    ap.add_argument("--steps-per-block", type=int, default=32, help="diffusion steps per block (quota rule)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")

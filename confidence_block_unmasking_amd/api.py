@@ -61,12 +61,13 @@ def _logits_shape(logits, rows, L, V, pos_stride, row_stride):
 
 
 def _decide_args(rows, L, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status, p, b, conf,
-                 argmax):
+                 argmax, need_tau=True):
     W = input_ids.shape[-1]
     _need(input_ids, torch.int32, "input_ids", rows * W)
     _need(mask_in, torch.uint8, "mask_in", rows * L)
     _need(mask_out, torch.uint8, "mask_out", rows * L)
-    _need(threshold, torch.float32, "threshold", rows)
+    if need_tau:
+        _need(threshold, torch.float32, "threshold", rows)
     _need(done, torch.uint8, "done", rows)
     _need(accept_len, torch.int32, "accept_len", rows)
     _need(workspace, torch.uint8, "workspace")
@@ -120,6 +121,34 @@ def dllm_step_decide(dtype, rows, L, V, input_ids, mask_in, mask_out, threshold,
                                      _ptr(mask_out), _ptr(threshold), _ptr(p), _ptr(b), _ptr(conf), _ptr(argmax),
                                      _ptr(done), _ptr(accept_len), _ptr(workspace), workspace.numel(), _ptr(status))
     _lib.check(rc, "dllm_step_decide")
+
+
+def dllm_step_quota(logits, input_ids, mask_in, mask_out, steps_per_block, done, accept_len, workspace, status,
+                    p=None, b=None, conf=None, argmax=None, rows=None, L=None, V=None, pos_stride=None,
+                    row_stride=None, stream=None):
+    """One denoise step with the fixed per-step quota (steps_per_block diffusion steps per block)."""
+    rows, L, V, pos_stride, row_stride = _logits_shape(logits, rows, L, V, pos_stride, row_stride)
+    W = _decide_args(rows, L, input_ids, mask_in, mask_out, None, done, accept_len, workspace, status, p, b, conf,
+                     argmax, need_tau=False)
+    rc = _lib.lib().dllm_step_quota(_stream(stream), _ptr(logits), _DT[logits.dtype], pos_stride, row_stride, rows,
+                                    L, V, _ptr(input_ids), W, _ptr(mask_in), _ptr(mask_out), int(steps_per_block),
+                                    _ptr(p), _ptr(b), _ptr(conf), _ptr(argmax), _ptr(done), _ptr(accept_len),
+                                    _ptr(workspace), workspace.numel(), _ptr(status))
+    _lib.check(rc, "dllm_step_quota")
+
+
+def dllm_step_decide_quota(dtype, rows, L, V, input_ids, mask_in, mask_out, steps_per_block, done, accept_len,
+                           workspace, status, p=None, b=None, conf=None, argmax=None, stream=None):
+    """The deciding half of dllm_step_quota, on the partials dllm_step_score left in `workspace`."""
+    if dtype not in _DT:
+        raise ValueError(f"dtype {dtype} not supported")
+    W = _decide_args(rows, L, input_ids, mask_in, mask_out, None, done, accept_len, workspace, status, p, b, conf,
+                     argmax, need_tau=False)
+    rc = _lib.lib().dllm_step_decide_quota(_stream(stream), _DT[dtype], rows, L, V, _ptr(input_ids), W,
+                                           _ptr(mask_in), _ptr(mask_out), int(steps_per_block), _ptr(p), _ptr(b),
+                                           _ptr(conf), _ptr(argmax), _ptr(done), _ptr(accept_len), _ptr(workspace),
+                                           workspace.numel(), _ptr(status))
+    _lib.check(rc, "dllm_step_decide_quota")
 
 
 class ReqTable:

@@ -65,6 +65,7 @@ struct StepParams {
     const float *tau;
     const int32_t *p, *b;                     // never NULL here (see check_fit)
     int32_t check_fit;                        // p and b were given: check p + (b+1)L <= W
+    int32_t S;                                // quota rule: diffusion steps per block (0: threshold rule)
     float *conf_out;
     int32_t *arg_out;
     uint8_t *done;
@@ -428,11 +429,28 @@ __device__ __forceinline__ void merge_lanes(const float4 &t, bool valid, float &
     Sb = red_sum(mc == -INFINITY ? 0.0f : sc * __builtin_amdgcn_exp2f((mc - Mb) * kLog2e));
 }
 
+// Quota of the step at which m of a block's L slots are still masked, for S steps per block:
+// step t takes floor(L/S) tokens and the first L mod S steps one more ([BlockServe] §II-E); the
+// step is the last one whose running total of unmasked tokens P_t = t*base + min(t, rem) does
+// not exceed L - m; past step S every remaining slot goes.
+__device__ __forceinline__ int quota_for_remaining(int L, int S, int m) {
+    if (m <= 0) return 0;
+    const int base = L / S, rem = L - base * S, u = L - m;
+    int t;
+    if (u < rem * (base + 1)) t = u / (base + 1);
+    else t = base > 0 ? rem + (u - rem * (base + 1)) / base : S;
+    if (t >= S) return m;
+    return min(m, base + (t < rem ? 1 : 0));
+}
+
 // Kernel 2: one workgroup per row.  Merge each masked slot's NC partials in chunk order (lanes =
-// chunks, a fixed DPP tree, then blocks of 64 chunks in order), then the LowConfidence rule.
+// chunks, a fixed DPP tree, then blocks of 64 chunks in order), then the row's rule: LowConfidence
+// (QUOTA false) or the fixed per-step quota (QUOTA true: the k most confident masked slots, k from
+// quota_for_remaining, ties to the lowest j).
 // Each wave loads the partials and mask bytes of kGroup slots before reducing any of them, so a
 // row costs about one memory round trip; partials of unmasked slots are loaded but never used.
 // A row's mask bytes are read before any of its outputs is written, so mask_out may be mask_in.
+template <bool QUOTA>
 __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
     extern __shared__ float s_conf[];           // [L]
     const int row = blockIdx.x;
@@ -441,6 +459,7 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
     const int L = P.L, NC = P.NC;
     int *s_arg = (int *)(s_conf + L);           // [L]
     uint8_t *s_mask = (uint8_t *)(s_arg + L);   // [L]
+    uint8_t *s_u = s_mask + L;                  // [L] quota rule: slot unmasked this step
     const uint8_t *mrow = P.mask_in + (int64_t)row * L;
     const float4 *prow = P.partials + (int64_t)row * L * NC;
     // inputs of the rule first (lanes 0, 1, 2: tau, p, b; one vector load), so that their
@@ -492,31 +511,52 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
         }
     }
     __syncthreads();
+    int nmasked = 0;
+    if (QUOTA) {
+        // every thread: the masked count and k; then the rank of each of its masked slots among the
+        // row's masked slots by (confidence descending, slot ascending); rank < k unmasks
+        for (int g = 0; g < L; g += 64) nmasked += __popcll(__ballot(g + lane < L && s_mask[g + lane]));
+        const int k = quota_for_remaining(L, P.S, nmasked);
+        for (int j = tid; j < L; j += kDecideThreads) {
+            bool u = false;
+            if (s_mask[j]) {
+                const float cj = s_conf[j];
+                int rank = 0;
+                for (int i = 0; i < L; ++i)
+                    rank += s_mask[i] && (s_conf[i] > cj || (s_conf[i] == cj && i < j));
+                u = rank < k;
+            }
+            s_u[j] = u;
+        }
+        __syncthreads();
+    }
     if (wave != 0) return;
-    // the rule, on wave 0: U = {masked j : c_j > tau}; if empty, the masked j with the largest c
-    // (lowest j on ties)
     const float tau = __int_as_float(__builtin_amdgcn_readlane(rule_in, 0));
     const int32_t p_r = __builtin_amdgcn_readlane(rule_in, 1), b_r = __builtin_amdgcn_readlane(rule_in, 2);
     if (lane == 0 && P.check_fit && (int64_t)p_r + ((int64_t)b_r + 1) * L > P.W) set_status(P.status, DLLM_ERR_SHAPE);
+    // the threshold rule, on wave 0: U = {masked j : c_j > tau}; if empty, the masked j with the
+    // largest c (lowest j on ties)
     bool any_above = false;
-    float best_c = -INFINITY;
-    int best_j = 0x7FFFFFFF, nmasked = 0;
-    for (int g = 0; g < L; g += 64) {
-        const int j = g + lane;
-        const bool masked = j < L && s_mask[j];
-        const float c = masked ? s_conf[j] : -INFINITY;
-        any_above |= __ballot(masked && c > tau) != 0;
-        nmasked += __popcll(__ballot(masked));
-        const float gmx = wave_max(c);
-        const int gj = wave_min((masked && c == gmx) ? j : 0x7FFFFFFF);
-        if (gmx > best_c) { best_c = gmx; best_j = gj; }        // earlier groups win ties
+    int best_j = 0x7FFFFFFF;
+    if (!QUOTA) {
+        float best_c = -INFINITY;
+        for (int g = 0; g < L; g += 64) {
+            const int j = g + lane;
+            const bool masked = j < L && s_mask[j];
+            const float c = masked ? s_conf[j] : -INFINITY;
+            any_above |= __ballot(masked && c > tau) != 0;
+            nmasked += __popcll(__ballot(masked));
+            const float gmx = wave_max(c);
+            const int gj = wave_min((masked && c == gmx) ? j : 0x7FFFFFFF);
+            if (gmx > best_c) { best_c = gmx; best_j = gj; }        // earlier groups win ties
+        }
     }
     int n_unmasked = 0;
     const int col0 = P.W - L;
     for (int g = 0; g < L; g += 64) {
         const int j = g + lane;
         const bool masked = j < L && s_mask[j];
-        const bool u = masked && (any_above ? (s_conf[j] > tau) : (j == best_j));
+        const bool u = masked && (QUOTA ? s_u[j] != 0 : any_above ? (s_conf[j] > tau) : (j == best_j));
         n_unmasked += __popcll(__ballot(u));
         if (j < L) {
             const int64_t qi = (int64_t)row * L + j;
@@ -591,14 +631,19 @@ dllm_status check_score(const char *who, const void *logits, dllm_dtype dtype, i
     return DLLM_OK;
 }
 
+// steps = 0: the threshold rule (threshold required); steps >= 1: the quota rule with that many
+// diffusion steps per block (threshold unused).
 dllm_status check_decide(const char *who, int32_t *input_ids, int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
-                         const float *threshold, const int32_t *p, const int32_t *b, float *conf, int32_t *argmax,
-                         uint8_t *done, int32_t *accept_len, int32_t *status, StepParams &P) {
+                         const float *threshold, int32_t steps, const int32_t *p, const int32_t *b, float *conf,
+                         int32_t *argmax, uint8_t *done, int32_t *accept_len, int32_t *status, StepParams &P) {
     if (W < P.L) return fail(DLLM_ERR_SHAPE, "%s: W=%d < L=%d", who, W, P.L);
     if ((p == nullptr) != (b == nullptr)) return fail(DLLM_ERR_ARG, "%s: p and b must be both given or both NULL", who);
+    if (steps < 0) return fail(DLLM_ERR_ARG, "%s: steps_per_block < 1", who);
+    P.S = steps;
     if (P.rows == 0) return DLLM_OK;
-    if (!input_ids || !mask_in || !mask_out || !threshold || !done || !accept_len || !status)
+    if (!input_ids || !mask_in || !mask_out || (steps == 0 && !threshold) || !done || !accept_len || !status)
         return fail(DLLM_ERR_ARG, "%s: null required pointer", who);
+    if (!threshold) threshold = (const float *)accept_len;   // never read for its value
     const int64_t S = (int64_t)P.rows * P.L;
     if (mask_out != mask_in && (uintptr_t)mask_out < (uintptr_t)mask_in + (uintptr_t)S &&
         (uintptr_t)mask_in < (uintptr_t)mask_out + (uintptr_t)S)
@@ -643,8 +688,9 @@ dllm_status launch_score(const StepParams &P, dllm_dtype dtype, hipStream_t st) 
 }
 
 dllm_status launch_decide(const StepParams &P, hipStream_t st) {
-    const size_t lds = (size_t)P.L * 9 + 16;
-    hipLaunchKernelGGL(decide_kernel, dim3((unsigned)P.rows), dim3(kDecideThreads), lds, st, P);
+    const size_t lds = (size_t)P.L * 10 + 16;
+    if (P.S > 0) hipLaunchKernelGGL(decide_kernel<true>, dim3((unsigned)P.rows), dim3(kDecideThreads), lds, st, P);
+    else hipLaunchKernelGGL(decide_kernel<false>, dim3((unsigned)P.rows), dim3(kDecideThreads), lds, st, P);
     return check_hip(hipGetLastError(), "dllm_step decide launch");
 }
 
@@ -667,7 +713,7 @@ extern "C" dllm_status dllm_step(void *stream, const void *logits, dllm_dtype dt
     dllm_status rc = check_shape("dllm_step", dtype, rows, L, V, workspace, P);
     if (rc == DLLM_OK) rc = check_score("dllm_step", logits, dtype, pos_stride, row_stride, mask_in, status, P);
     if (rc == DLLM_OK)
-        rc = check_decide("dllm_step", input_ids, W, mask_in, mask_out, threshold, p, b, conf, argmax, done,
+        rc = check_decide("dllm_step", input_ids, W, mask_in, mask_out, threshold, 0, p, b, conf, argmax, done,
                           accept_len, status, P);
     if (rc == DLLM_OK) rc = check_workspace("dllm_step", dtype, workspace, workspace_bytes, P);
     if (rc != DLLM_OK || rows == 0) return rc;
@@ -696,9 +742,46 @@ extern "C" dllm_status dllm_step_decide(void *stream, dllm_dtype dtype, int32_t 
     StepParams P{};
     dllm_status rc = check_shape("dllm_step_decide", dtype, rows, L, V, workspace, P);
     if (rc == DLLM_OK)
-        rc = check_decide("dllm_step_decide", input_ids, W, mask_in, mask_out, threshold, p, b, conf, argmax,
+        rc = check_decide("dllm_step_decide", input_ids, W, mask_in, mask_out, threshold, 0, p, b, conf, argmax,
                           done, accept_len, status, P);
     if (rc == DLLM_OK) rc = check_workspace("dllm_step_decide", dtype, workspace, workspace_bytes, P);
+    if (rc != DLLM_OK || rows == 0) return rc;
+    return launch_decide(P, (hipStream_t)stream);
+}
+
+extern "C" dllm_status dllm_step_quota(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+                                       int64_t row_stride, int32_t rows, int32_t L, int32_t V, int32_t *input_ids,
+                                       int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
+                                       int32_t steps_per_block, const int32_t *p, const int32_t *b, float *conf,
+                                       int32_t *argmax, uint8_t *done, int32_t *accept_len, void *workspace,
+                                       size_t workspace_bytes, int32_t *status) {
+    StepParams P{};
+    if (steps_per_block < 1) return fail(DLLM_ERR_ARG, "dllm_step_quota: steps_per_block < 1");
+    dllm_status rc = check_shape("dllm_step_quota", dtype, rows, L, V, workspace, P);
+    if (rc == DLLM_OK) rc = check_score("dllm_step_quota", logits, dtype, pos_stride, row_stride, mask_in, status, P);
+    if (rc == DLLM_OK)
+        rc = check_decide("dllm_step_quota", input_ids, W, mask_in, mask_out, nullptr, steps_per_block, p, b, conf,
+                          argmax, done, accept_len, status, P);
+    if (rc == DLLM_OK) rc = check_workspace("dllm_step_quota", dtype, workspace, workspace_bytes, P);
+    if (rc != DLLM_OK || rows == 0) return rc;
+    rc = launch_score(P, dtype, (hipStream_t)stream);
+    if (rc != DLLM_OK) return rc;
+    return launch_decide(P, (hipStream_t)stream);
+}
+
+extern "C" dllm_status dllm_step_decide_quota(void *stream, dllm_dtype dtype, int32_t rows, int32_t L, int32_t V,
+                                              int32_t *input_ids, int32_t W, const uint8_t *mask_in,
+                                              uint8_t *mask_out, int32_t steps_per_block, const int32_t *p,
+                                              const int32_t *b, float *conf, int32_t *argmax, uint8_t *done,
+                                              int32_t *accept_len, void *workspace, size_t workspace_bytes,
+                                              int32_t *status) {
+    StepParams P{};
+    if (steps_per_block < 1) return fail(DLLM_ERR_ARG, "dllm_step_decide_quota: steps_per_block < 1");
+    dllm_status rc = check_shape("dllm_step_decide_quota", dtype, rows, L, V, workspace, P);
+    if (rc == DLLM_OK)
+        rc = check_decide("dllm_step_decide_quota", input_ids, W, mask_in, mask_out, nullptr, steps_per_block, p, b,
+                          conf, argmax, done, accept_len, status, P);
+    if (rc == DLLM_OK) rc = check_workspace("dllm_step_decide_quota", dtype, workspace, workspace_bytes, P);
     if (rc != DLLM_OK || rows == 0) return rc;
     return launch_decide(P, (hipStream_t)stream);
 }

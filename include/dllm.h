@@ -153,6 +153,27 @@ dllm_status dllm_step_decide(void *stream, dllm_dtype dtype, int32_t rows, int32
                              int32_t *argmax, uint8_t *done, int32_t *accept_len, void *workspace,
                              size_t workspace_bytes, int32_t *status);
 
+/* dllm_step_quota and dllm_step_decide_quota — the step (and its deciding half) with the fixed
+ * per-step quota of [BlockServe] §II-E (向量化混合调度执行: the per-step transfer quota spreads a
+ * block's masked tokens evenly over S diffusion steps; §III-A: S = 32 for L = 32) in place of the
+ * threshold.  Confidence and predicted token are those of dllm_step.  Per row with m masked slots:
+ *   base = L / S, rem = L % S; step t of a block takes base + (t < rem) tokens;
+ *   t = the last step whose running total t*base + min(t, rem) does not exceed L - m;
+ *   k = m if t >= S, else min(m, base + (t < rem));
+ *   U = the k masked slots with the largest confidence, the lowest j on ties.
+ * Write-back, done and accept_len as for dllm_step.  steps_per_block >= 1 (DLLM_ERR_ARG
+ * otherwise); no threshold.  Other arguments and errors as for dllm_step / dllm_step_decide. */
+dllm_status dllm_step_quota(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+                            int64_t row_stride, int32_t rows, int32_t L, int32_t V, int32_t *input_ids,
+                            int32_t W, const uint8_t *mask_in, uint8_t *mask_out, int32_t steps_per_block,
+                            const int32_t *p, const int32_t *b, float *conf, int32_t *argmax, uint8_t *done,
+                            int32_t *accept_len, void *workspace, size_t workspace_bytes, int32_t *status);
+dllm_status dllm_step_decide_quota(void *stream, dllm_dtype dtype, int32_t rows, int32_t L, int32_t V,
+                                   int32_t *input_ids, int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
+                                   int32_t steps_per_block, const int32_t *p, const int32_t *b, float *conf,
+                                   int32_t *argmax, uint8_t *done, int32_t *accept_len, void *workspace,
+                                   size_t workspace_bytes, int32_t *status);
+
 /* dllm_pack — materialise the left-padded bounding box for the active rows.
  *
  * Defined by [BlockServe] §II-D Eq.(1) (row width p_i + (b_i + 1) L) and §II-E 逻辑位置对齐 (a dense

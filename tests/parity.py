@@ -11,6 +11,7 @@ Everything integer (ids, masks, done, accept, pack/compact layouts) is compared 
 """
 import numpy as np
 
+from oracle import quota as oquota
 from oracle import step as ostep
 
 CONF_TOL = 1e-5
@@ -53,3 +54,30 @@ def check_scores(gpu_conf, gpu_arg, oracle_conf, oracle_arg, where=None):
     err = np.abs(np.asarray(gpu_conf, np.float64)[sel] - oracle_conf[sel])
     assert err.size == 0 or err.max() <= CONF_TOL, f"conf error {err.max()}"
     return float(err.max()) if err.size else 0.0
+
+
+def ambiguous_topk_row(conf_row, masked, k):
+    """Quota rule: ambiguous when the k-th and (k+1)-th largest masked oracle confidences (the cut)
+    are within CONF_TOL."""
+    c = np.sort(np.asarray(conf_row, np.float64)[masked])[::-1]
+    if k <= 0 or k >= c.size:
+        return False
+    return bool(c[k - 1] - c[k] <= CONF_TOL)
+
+
+def check_quota_decisions(gpu_conf, oracle_conf, mask_in, mask_out_gpu, S):
+    """(iii) and (iv) for the quota rule; returns the number of ambiguous rows."""
+    rows, L = mask_in.shape
+    n_amb = 0
+    for r in range(rows):
+        masked = mask_in[r] != 0
+        k = oquota.quota_for_remaining(L, S, int(masked.sum()))
+        gpu_U = masked & (mask_out_gpu[r] == 0)
+        own = oquota.decide_topk(np.asarray(gpu_conf[r], np.float64), masked, k)
+        assert np.array_equal(gpu_U, own), f"row {r}: decision differs from the quota rule on the GPU's confidences"
+        if ambiguous_topk_row(oracle_conf[r], masked, k):
+            n_amb += 1
+            continue
+        ref = oquota.decide_topk(np.asarray(oracle_conf[r], np.float64), masked, k)
+        assert np.array_equal(gpu_U, ref), f"row {r}: quota decision differs from the oracle's"
+    return n_amb

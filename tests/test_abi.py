@@ -109,6 +109,27 @@ def test_step_halves_reject_bad_arguments():
     assert decide(rows=0, ids=None) == _lib.DLLM_OK
 
 
+def test_quota_rejects_bad_arguments():
+    L = _lib.lib()
+    need = L.dllm_step_workspace_bytes(4, 32, 1024, 1)
+    f, ws = FAKE, ctypes.c_void_p(0x10000)
+
+    def quota(S=32, done=f, W=40, rows=4):
+        return L.dllm_step_quota(None, f, 1, 1024, 32 * 1024, rows, 32, 1024, f, W, f, ctypes.c_void_p(0x2000), S,
+                                 None, None, None, None, done, f, ws, need, f)
+
+    def dq(S=32, done=f):
+        return L.dllm_step_decide_quota(None, 1, 4, 32, 1024, f, 40, f, ctypes.c_void_p(0x2000), S, None, None,
+                                        None, None, done, f, ws, need, f)
+    assert quota(S=0) == _lib.DLLM_ERR_ARG
+    assert quota(S=-3) == _lib.DLLM_ERR_ARG
+    assert quota(done=None) == _lib.DLLM_ERR_ARG
+    assert quota(W=31) == _lib.DLLM_ERR_SHAPE
+    assert quota(rows=0) == _lib.DLLM_OK
+    assert dq(S=0) == _lib.DLLM_ERR_ARG
+    assert dq(done=None) == _lib.DLLM_ERR_ARG
+
+
 def test_step_rows_zero_is_noop():
     assert _step(rows=0, logits=None, ids=None) == _lib.DLLM_OK
 
