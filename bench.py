@@ -34,15 +34,19 @@ sys.path.insert(0, ROOT)
 METRIC = "masked positions scored/sec + logits HBM GB/s (fraction of MI355X peak), 1 GPU"
 PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_dream_dynamic_traffic.json")
-STEP_SRC = os.path.join(ROOT, "confidence_block_unmasking_amd", "csrc", "step.hip")
+# the scoring kernel's sources: the traffic figure is reported only while these are unchanged
+SCORE_SRC = [os.path.join(ROOT, "confidence_block_unmasking_amd", "csrc", f) for f in ("score.hip", "step_common.h")]
 SCORE_KERNEL = "score_kernel"
 COPY_MIB = 256
 EV_EVERY = 8          # steps between two HIP-event samples of the scoring kernel
 
 
-def _sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def _sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 # ---- CPU baseline: the float64 oracle as it stands, on host cores ------------------------------
@@ -147,7 +151,7 @@ def record_traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, masked):
     cw_kib, _ = _per_dispatch(_pmc_rows(cwrite_dir), is_copy, "WRITE_SIZE")
     sf, sw = known_kib / cf_kib, known_kib / cw_kib
     rec = {"kernel": SCORE_KERNEL, "workload": "Dream-shaped dynamic-threshold step (64 x 32 x 152064 bf16)",
-           "masked_positions": masked, "source_sha256": _sha(STEP_SRC),
+           "masked_positions": masked, "source_sha256": _sha(SCORE_SRC),
            "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
            "copy_mib": COPY_MIB, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
            "fetch_scale": sf, "write_scale": sw,
@@ -163,7 +167,7 @@ def stored_traffic(masked):
         return None
     with open(TRAFFIC_FILE) as f:
         tr = json.load(f)
-    if tr.get("source_sha256") != _sha(STEP_SRC) or tr.get("masked_positions") != masked:
+    if tr.get("source_sha256") != _sha(SCORE_SRC) or tr.get("masked_positions") != masked:
         return None                       # the kernel changed since the counters were taken
     return tr.get("hbm_bytes_per_launch")
 

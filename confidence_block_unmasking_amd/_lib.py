@@ -18,7 +18,7 @@ DLLM_FP32, DLLM_BF16 = 0, 1
 MAX_L, MAX_ROWS, MAX_POSITIONS, MAX_QUEUE = 1024, 4096, 262144, 8192
 
 EXPORTS = ("dllm_step", "dllm_step_score", "dllm_step_decide", "dllm_step_quota", "dllm_step_decide_quota",
-           "dllm_step_workspace_bytes", "dllm_pack", "dllm_compact", "dllm_last_error")
+           "dllm_step_features", "dllm_step_workspace_bytes", "dllm_pack", "dllm_compact", "dllm_last_error")
 
 
 class DllmError(RuntimeError):
@@ -71,6 +71,8 @@ def lib():
         L.dllm_step_decide_quota.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp,
                                              vp, vp, vp, sz, vp]
         L.dllm_step_decide_quota.restype = ctypes.c_int
+        L.dllm_step_features.argtypes = [vp, i32, i32, vp, ctypes.POINTER(Reqs), vp, vp, vp, vp]
+        L.dllm_step_features.restype = ctypes.c_int
         L.dllm_step_workspace_bytes.argtypes = [i32, i32, i32, ctypes.c_int]
         L.dllm_step_workspace_bytes.restype = sz
         L.dllm_pack.argtypes = [vp, i32, i32, i32, i32, vp, ctypes.POINTER(Reqs), vp, vp, vp, vp, vp, vp, vp, vp]

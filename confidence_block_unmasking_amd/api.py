@@ -151,6 +151,22 @@ def dllm_step_decide_quota(dtype, rows, L, V, input_ids, mask_in, mask_out, step
     _lib.check(rc, "dllm_step_decide_quota")
 
 
+N_FEATURES = 9
+
+
+def dllm_step_features(rows, L, row_req, reqs: "ReqTable", conf, mask_out, features, status, stream=None):
+    """Step-predictor features per row after a step: float32 [rows, 9] (see include/dllm.h)."""
+    _need(row_req, torch.int32, "row_req", rows)
+    _need(conf, torch.float32, "conf", rows * L)
+    _need(mask_out, torch.uint8, "mask_out", rows * L)
+    _need(features, torch.float32, "features", rows * N_FEATURES)
+    _need(status, torch.int32, "status", 1)
+    st = reqs.struct()
+    rc = _lib.lib().dllm_step_features(_stream(stream), rows, L, _ptr(row_req), ctypes.byref(st), _ptr(conf),
+                                       _ptr(mask_out), _ptr(features), _ptr(status))
+    _lib.check(rc, "dllm_step_features")
+
+
 class ReqTable:
     """Device-resident request table (the fields of dllm_reqs), built from host numpy arrays."""
 

@@ -58,6 +58,7 @@ class Session:
         self.workspace = api.new_workspace(n, self.L, self.V, dtype, device=device)
         self.status = torch.zeros(1, dtype=i32, device=device)
         self.meta = torch.zeros(32, dtype=u8, device=device)
+        self.features_buf = torch.empty(n * api.N_FEATURES, dtype=f32, device=device)
         self.logits = logits if logits is not None else torch.empty((n, self.L, self.V), dtype=dtype, device=device)
         self.W = 0
         self.stats = dict(steps=0, positions_scored=0, compacts=0, packs=0, idle_request_steps=0, max_cost=0,
@@ -119,6 +120,12 @@ class Session:
             ev[1].record()
             self.step_events.append(ev)
         self.cur = nxt
+
+    def features(self):
+        """Step-predictor features of the current rows after the last step: device [rows, 9]."""
+        api.dllm_step_features(self.rows, self.L, self.row_req, self.reqs, self.conf, self.masks[self.cur],
+                               self.features_buf, self.status)
+        return self.features_buf[:self.rows * api.N_FEATURES].view(self.rows, api.N_FEATURES)
 
     # ---- the loop rule ----------------------------------------------------------------------------
     def run(self, mode, forward, max_steps=10**7, on_step=None, timed=False):

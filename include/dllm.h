@@ -174,6 +174,28 @@ dllm_status dllm_step_decide_quota(void *stream, dllm_dtype dtype, int32_t rows,
                                    int32_t *argmax, uint8_t *done, int32_t *accept_len, void *workspace,
                                    size_t workspace_bytes, int32_t *status);
 
+/* dllm_step_features — per-request inputs of a remaining-step predictor, after a step.
+ *
+ * Defined by [DiLaServe] §四 4.2 ③ (paper §3.2.3, Step Prediction): progress features (the
+ * fraction of tokens already unmasked) and confidence features (quantiles of the output tokens'
+ * confidences); the page names the threshold, output length, full and block progress and the
+ * min / q25 / median / mean / q75 confidence (it counts 11, these 9 are the ones it names).  The
+ * predictor itself (a trained model) is not part of this library.
+ *
+ * For row r holding request q = row_req[r]:
+ *   features[r, 0..8] (float32) = { threshold[q], K[q]*L, (b[q]*L + u)/(K[q]*L), u/L,
+ *                                   min c, q25 c, median c, mean c, q75 c }
+ * with u = slots of the row's block unmasked after the step (L minus the nonzero mask_out bytes)
+ * and c the confidences the step scored (conf >= 0; conf as written by dllm_step).  Quantiles
+ * interpolate linearly between order statistics at position q*(n-1); with no scored slot the five
+ * confidence features are NaN.  b[q] is the current block (call before dllm_compact).
+ * row_req: int32 [rows]; conf: float32 [rows, L]; mask_out: uint8 [rows, L]; features: float32
+ * [rows, 9].  Errors: DLLM_ERR_ARG (null pointer, incomplete table; on the device *status for a
+ * bad request id, whose row reads NaN), DLLM_ERR_SHAPE (L or rows out of range). */
+dllm_status dllm_step_features(void *stream, int32_t rows, int32_t L, const int32_t *row_req,
+                               const dllm_reqs *reqs, const float *conf, const uint8_t *mask_out,
+                               float *features, int32_t *status);
+
 /* dllm_pack — materialise the left-padded bounding box for the active rows.
  *
  * Defined by [BlockServe] §II-D Eq.(1) (row width p_i + (b_i + 1) L) and §II-E 逻辑位置对齐 (a dense

@@ -130,6 +130,23 @@ def test_quota_rejects_bad_arguments():
     assert dq(done=None) == _lib.DLLM_ERR_ARG
 
 
+def test_features_rejects_bad_arguments():
+    L = _lib.lib()
+    r = _reqs()
+    f = FAKE
+
+    def call(rows=4, Lb=32, row_req=f, reqs=r, conf=f, mask=f, out=f, status=f):
+        return L.dllm_step_features(None, rows, Lb, row_req, ctypes.byref(reqs) if reqs is not None else None, conf,
+                                    mask, out, status)
+    assert call(rows=-1) == _lib.DLLM_ERR_ARG
+    assert call(Lb=0) == _lib.DLLM_ERR_SHAPE
+    assert call(rows=5000) == _lib.DLLM_ERR_SHAPE
+    assert call(conf=None) == _lib.DLLM_ERR_ARG
+    assert call(reqs=None) == _lib.DLLM_ERR_ARG
+    assert call(reqs=_lib.Reqs(4, 0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)) == _lib.DLLM_ERR_ARG
+    assert call(rows=0, row_req=None, conf=None) == _lib.DLLM_OK
+
+
 def test_step_rows_zero_is_noop():
     assert _step(rows=0, logits=None, ids=None) == _lib.DLLM_OK
 

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import compact as ocompact
+from oracle import features as ofeat
 from oracle import loop as oloop
 from oracle import pack as opack
 from oracle import step as ostep
@@ -58,7 +59,16 @@ def gpu_forward(w):
     return fwd
 
 
-def lockstep_run(w, full_score_max=64, sample=16, whole_rows=1, deep_every=1, seed=0, label="", eos_id=-1):
+def _check_features(sess, st, rows, L, g_conf, g_mask):
+    """dllm_step_features against the oracle's, from the GPU's own confidences and masks."""
+    g = sess.features().cpu().numpy().astype(np.float64)
+    rr = st["row_req"][:rows]
+    o = ofeat.features(g_conf.astype(np.float64), g_mask, st["threshold"][rr], st["b"][rr], st["K"][rr], L)
+    assert np.allclose(g, o, rtol=0, atol=1e-6, equal_nan=True), np.abs(g - o).max()
+
+
+def lockstep_run(w, full_score_max=64, sample=16, whole_rows=1, deep_every=1, seed=0, label="", eos_id=-1,
+                 features_every=1):
     from confidence_block_unmasking_amd.driver import Session
     rng = np.random.default_rng(seed)
     sess = Session.from_workload(w, eos_id=eos_id)
@@ -139,6 +149,8 @@ def lockstep_run(w, full_score_max=64, sample=16, whole_rows=1, deep_every=1, se
             assert np.array_equal(g_mask, mask_o), "mask"
             assert np.array_equal(g_done, done_o), "done"
             assert np.array_equal(g_acc, np.where(done_o == 1, L, 0)), "accept"
+            if n_steps % features_every == 0:
+                _check_features(sess, st, rows, L, g_conf, g_mask)
             if w.mode == "fdfo" and done_o.any():
                 break
             if w.mode == "sync" and done_o.all():
@@ -217,8 +229,10 @@ def test_loop_config2_sync():
 
 
 def test_loop_config4_fdfo():
-    lockstep_run(configs.config4(), full_score_max=0, sample=4, whole_rows=0, deep_every=5, label="c4")
+    lockstep_run(configs.config4(), full_score_max=0, sample=4, whole_rows=0, deep_every=5, label="c4",
+                 features_every=10)
 
 
 def test_loop_config5_fdfo():
-    lockstep_run(configs.config5(), full_score_max=0, sample=2, whole_rows=0, deep_every=25, label="c5")
+    lockstep_run(configs.config5(), full_score_max=0, sample=2, whole_rows=0, deep_every=25, label="c5",
+                 features_every=25)

@@ -18,6 +18,7 @@ STEP = "tests/test_oracle_step.py"
 PACK = "tests/test_oracle_pack_compact.py"
 LOOP = "tests/test_oracle_loop.py"
 QUOTA = "tests/test_oracle_quota.py"
+FEAT = "tests/test_oracle_features.py"
 
 MUTATIONS = [
     ("oracle/step.py", "S = float(np.sum(np.exp(x - m)))", "S = float(np.sum(np.exp(m - x)))", STEP),
@@ -44,6 +45,9 @@ MUTATIONS = [
     ("oracle/quota.py", "js.sort(key=lambda j: (-float(conf[j]), j))", "js.sort(key=lambda j: (-float(conf[j]), -j))",
      QUOTA),
     ("oracle/quota.py", "while t < S and pre + ks[t] <= u:", "while t < S and pre + ks[t] < u:", QUOTA),
+    ("oracle/features.py", "f[2] = (b * L + unmasked) / (K * L)", "f[2] = ((b + 1) * L + unmasked) / (K * L)", FEAT),
+    ("oracle/features.py", "f[5], f[6], f[8] = np.quantile(c, [0.25, 0.5, 0.75])",
+     "f[5], f[6], f[8] = np.quantile(c, [0.25, 0.5, 0.75], method='lower')", FEAT),
 ]
 
 
@@ -63,7 +67,7 @@ def _run_pins(dst, pin_file):
 
 def test_unmodified_copy_passes(tmp_path):
     _copy_tree(str(tmp_path))
-    for pin in (STEP, PACK, LOOP, QUOTA):
+    for pin in (STEP, PACK, LOOP, QUOTA, FEAT):
         r = _run_pins(str(tmp_path), pin)
         assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
 
