@@ -18,7 +18,8 @@ DLLM_FP32, DLLM_BF16 = 0, 1
 MAX_L, MAX_ROWS, MAX_POSITIONS, MAX_QUEUE = 1024, 4096, 262144, 8192
 
 EXPORTS = ("dllm_step", "dllm_step_score", "dllm_step_decide", "dllm_step_quota", "dllm_step_decide_quota",
-           "dllm_step_features", "dllm_step_workspace_bytes", "dllm_pack", "dllm_compact", "dllm_last_error")
+           "dllm_step_features", "dllm_step_score_shard", "dllm_step_decide_shards", "dllm_shard_triples_bytes",
+           "dllm_step_workspace_bytes", "dllm_pack", "dllm_compact", "dllm_last_error")
 
 
 class DllmError(RuntimeError):
@@ -73,6 +74,14 @@ def lib():
         L.dllm_step_decide_quota.restype = ctypes.c_int
         L.dllm_step_features.argtypes = [vp, i32, i32, vp, ctypes.POINTER(Reqs), vp, vp, vp, vp]
         L.dllm_step_features.restype = ctypes.c_int
+        L.dllm_shard_triples_bytes.argtypes = [i32, i32, i32]
+        L.dllm_shard_triples_bytes.restype = sz
+        L.dllm_step_score_shard.argtypes = [vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, i32, i32, i32, vp, vp, sz,
+                                            vp, vp]
+        L.dllm_step_score_shard.restype = ctypes.c_int
+        L.dllm_step_decide_shards.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              vp]
+        L.dllm_step_decide_shards.restype = ctypes.c_int
         L.dllm_step_workspace_bytes.argtypes = [i32, i32, i32, ctypes.c_int]
         L.dllm_step_workspace_bytes.restype = sz
         L.dllm_pack.argtypes = [vp, i32, i32, i32, i32, vp, ctypes.POINTER(Reqs), vp, vp, vp, vp, vp, vp, vp, vp]

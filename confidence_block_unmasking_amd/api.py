@@ -151,6 +151,40 @@ def dllm_step_decide_quota(dtype, rows, L, V, input_ids, mask_in, mask_out, step
     _lib.check(rc, "dllm_step_decide_quota")
 
 
+def new_triples(rows: int, L: int, n_shards: int, device="cuda"):
+    """Buffer for the per-shard results of dllm_step_score_shard ([rows, L, n_shards] records of 16 B)."""
+    n = _lib.lib().dllm_shard_triples_bytes(rows, L, n_shards)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def dllm_step_score_shard(logits, mask_in, workspace, triples, shard, n_shards, vocab_offset, status, rows=None,
+                          L=None, V_shard=None, pos_stride=None, row_stride=None, stream=None):
+    """Score one vocabulary shard (columns vocab_offset .. + V_shard - 1) of every masked slot."""
+    rows, L, V_shard, pos_stride, row_stride = _logits_shape(logits, rows, L, V_shard, pos_stride, row_stride)
+    _need(mask_in, torch.uint8, "mask_in", rows * L)
+    _need(workspace, torch.uint8, "workspace")
+    _need(triples, torch.uint8, "triples", _lib.lib().dllm_shard_triples_bytes(rows, L, n_shards))
+    _need(status, torch.int32, "status", 1)
+    rc = _lib.lib().dllm_step_score_shard(_stream(stream), _ptr(logits), _DT[logits.dtype], pos_stride, row_stride,
+                                          rows, L, V_shard, int(vocab_offset), int(shard), int(n_shards),
+                                          _ptr(mask_in), _ptr(workspace), workspace.numel(), _ptr(triples),
+                                          _ptr(status))
+    _lib.check(rc, "dllm_step_score_shard")
+
+
+def dllm_step_decide_shards(n_shards, triples, rows, L, V, input_ids, mask_in, mask_out, threshold, done, accept_len,
+                            status, p=None, b=None, conf=None, argmax=None, stream=None):
+    """Combine the shards' results per masked slot and apply the LowConfidence rule."""
+    W = _decide_args(rows, L, input_ids, mask_in, mask_out, threshold, done, accept_len, triples, status, p, b, conf,
+                     argmax)
+    _need(triples, torch.uint8, "triples", _lib.lib().dllm_shard_triples_bytes(rows, L, n_shards))
+    rc = _lib.lib().dllm_step_decide_shards(_stream(stream), int(n_shards), _ptr(triples), rows, L, V,
+                                            _ptr(input_ids), W, _ptr(mask_in), _ptr(mask_out), _ptr(threshold),
+                                            _ptr(p), _ptr(b), _ptr(conf), _ptr(argmax), _ptr(done), _ptr(accept_len),
+                                            _ptr(status))
+    _lib.check(rc, "dllm_step_decide_shards")
+
+
 N_FEATURES = 9
 
 

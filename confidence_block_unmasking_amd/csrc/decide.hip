@@ -43,8 +43,9 @@ __device__ __forceinline__ int quota_for_remaining(int L, int S, int m) {
 // Each wave loads the partials and mask bytes of kGroup slots before reducing any of them, so a
 // row costs about one memory round trip; partials of unmasked slots are loaded but never used.
 // A row's mask bytes are read before any of its outputs is written, so mask_out may be mask_in.
-template <bool QUOTA>
+template <int MODE>
 __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
+    constexpr bool QUOTA = MODE == kRuleQuota;
     extern __shared__ float s_conf[];           // [L]
     const int row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -57,8 +58,9 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
     const float4 *prow = P.partials + (int64_t)row * L * NC;
     // inputs of the rule first (lanes 0, 1, 2: tau, p, b; one vector load), so that their
     // latency overlaps that of the partials
+    // (no rule, and no rule inputs, when emitting shard results)
     const int32_t *rin = lane == 1 ? P.p : lane == 2 ? P.b : (const int32_t *)P.tau;
-    const int32_t rule_in = rin[row];
+    const int32_t rule_in = MODE == kEmitTriples ? 0 : rin[row];
     for (int g0 = wave; g0 < L; g0 += kDecideWaves * kGroup) {
         // slots g0, g0 + 4, ..., g0 + 4*(kGroup-1) of this row; addresses are clamped into the
         // row so that every load is unconditional and they all go out together
@@ -90,6 +92,19 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
                 }
             }
         }
+        if (MODE == kEmitTriples) {
+            // one shard's result per masked slot, its index made global
+            if (lane == 0) {
+#pragma unroll
+                for (int s = 0; s < kGroup; ++s) {
+                    const int j = g0 + s * kDecideWaves;
+                    if (j < L && ((gm >> s) & 1))
+                        P.triples[((int64_t)row * L + j) * P.n_shards + P.shard] =
+                            make_float4(Mr[s], Sr[s], __int_as_float(vr[s] + P.vocab_offset), 0.0f);
+                }
+            }
+            continue;
+        }
         if (lane == 0) {
 #pragma unroll
             for (int s = 0; s < kGroup; ++s) {
@@ -103,6 +118,7 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
             }
         }
     }
+    if (MODE == kEmitTriples) return;
     __syncthreads();
     int nmasked = 0;
     if (QUOTA) {
@@ -168,10 +184,12 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
 }
 
 
-dllm_status launch_decide(const StepParams &P, hipStream_t st) {
+dllm_status launch_decide(const StepParams &P, hipStream_t st, int mode) {
     const size_t lds = (size_t)P.L * 10 + 16;
-    if (P.S > 0) hipLaunchKernelGGL(decide_kernel<true>, dim3((unsigned)P.rows), dim3(kDecideThreads), lds, st, P);
-    else hipLaunchKernelGGL(decide_kernel<false>, dim3((unsigned)P.rows), dim3(kDecideThreads), lds, st, P);
+    const dim3 grid((unsigned)P.rows), block(kDecideThreads);
+    if (mode == kRuleQuota) hipLaunchKernelGGL(decide_kernel<kRuleQuota>, grid, block, lds, st, P);
+    else if (mode == kEmitTriples) hipLaunchKernelGGL(decide_kernel<kEmitTriples>, grid, block, lds, st, P);
+    else hipLaunchKernelGGL(decide_kernel<kRuleThreshold>, grid, block, lds, st, P);
     return check_hip(hipGetLastError(), "dllm_step decide launch");
 }
 

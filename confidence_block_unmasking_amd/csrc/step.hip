@@ -142,7 +142,7 @@ extern "C" dllm_status dllm_step(void *stream, const void *logits, dllm_dtype dt
     if (rc != DLLM_OK || rows == 0) return rc;
     rc = launch_score(P, dtype, (hipStream_t)stream);
     if (rc != DLLM_OK) return rc;
-    return launch_decide(P, (hipStream_t)stream);
+    return launch_decide(P, (hipStream_t)stream, P.S > 0 ? kRuleQuota : kRuleThreshold);
 }
 
 extern "C" dllm_status dllm_step_score(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
@@ -169,7 +169,7 @@ extern "C" dllm_status dllm_step_decide(void *stream, dllm_dtype dtype, int32_t 
                           done, accept_len, status, P);
     if (rc == DLLM_OK) rc = check_workspace("dllm_step_decide", dtype, workspace, workspace_bytes, P);
     if (rc != DLLM_OK || rows == 0) return rc;
-    return launch_decide(P, (hipStream_t)stream);
+    return launch_decide(P, (hipStream_t)stream, P.S > 0 ? kRuleQuota : kRuleThreshold);
 }
 
 extern "C" dllm_status dllm_step_quota(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
@@ -189,7 +189,7 @@ extern "C" dllm_status dllm_step_quota(void *stream, const void *logits, dllm_dt
     if (rc != DLLM_OK || rows == 0) return rc;
     rc = launch_score(P, dtype, (hipStream_t)stream);
     if (rc != DLLM_OK) return rc;
-    return launch_decide(P, (hipStream_t)stream);
+    return launch_decide(P, (hipStream_t)stream, P.S > 0 ? kRuleQuota : kRuleThreshold);
 }
 
 extern "C" dllm_status dllm_step_decide_quota(void *stream, dllm_dtype dtype, int32_t rows, int32_t L, int32_t V,
@@ -206,5 +206,55 @@ extern "C" dllm_status dllm_step_decide_quota(void *stream, dllm_dtype dtype, in
                           conf, argmax, done, accept_len, status, P);
     if (rc == DLLM_OK) rc = check_workspace("dllm_step_decide_quota", dtype, workspace, workspace_bytes, P);
     if (rc != DLLM_OK || rows == 0) return rc;
-    return launch_decide(P, (hipStream_t)stream);
+    return launch_decide(P, (hipStream_t)stream, P.S > 0 ? kRuleQuota : kRuleThreshold);
+}
+
+extern "C" size_t dllm_shard_triples_bytes(int32_t rows, int32_t L, int32_t n_shards) {
+    if (rows < 0 || L < 1 || n_shards < 1) return 0;
+    return (size_t)rows * (size_t)L * (size_t)n_shards * sizeof(float4);
+}
+
+extern "C" dllm_status dllm_step_score_shard(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+                                             int64_t row_stride, int32_t rows, int32_t L, int32_t V_shard,
+                                             int32_t vocab_offset, int32_t shard, int32_t n_shards,
+                                             const uint8_t *mask_in, void *workspace, size_t workspace_bytes,
+                                             void *triples, int32_t *status) {
+    StepParams P{};
+    dllm_status rc = check_shape("dllm_step_score_shard", dtype, rows, L, V_shard, workspace, P);
+    if (rc == DLLM_OK)
+        rc = check_score("dllm_step_score_shard", logits, dtype, pos_stride, row_stride, mask_in, status, P);
+    if (rc != DLLM_OK) return rc;
+    if (n_shards < 1 || n_shards > DLLM_MAX_SHARDS || shard < 0 || shard >= n_shards)
+        return fail(DLLM_ERR_ARG, "dllm_step_score_shard: shard %d of %d", shard, n_shards);
+    if (vocab_offset < 0 || (int64_t)vocab_offset + V_shard > INT32_MAX)
+        return fail(DLLM_ERR_ARG, "dllm_step_score_shard: vocab_offset %d", vocab_offset);
+    if (rows > 0 && !triples) return fail(DLLM_ERR_ARG, "dllm_step_score_shard: null triples");
+    rc = check_workspace("dllm_step_score_shard", dtype, workspace, workspace_bytes, P);
+    if (rc != DLLM_OK || rows == 0) return rc;
+    P.triples = (float4 *)triples;
+    P.shard = shard;
+    P.n_shards = n_shards;
+    P.vocab_offset = vocab_offset;
+    rc = launch_score(P, dtype, (hipStream_t)stream);
+    if (rc != DLLM_OK) return rc;
+    return launch_decide(P, (hipStream_t)stream, kEmitTriples);
+}
+
+extern "C" dllm_status dllm_step_decide_shards(void *stream, int32_t n_shards, const void *triples, int32_t rows,
+                                               int32_t L, int32_t V, int32_t *input_ids, int32_t W,
+                                               const uint8_t *mask_in, uint8_t *mask_out, const float *threshold,
+                                               const int32_t *p, const int32_t *b, float *conf, int32_t *argmax,
+                                               uint8_t *done, int32_t *accept_len, int32_t *status) {
+    StepParams P{};
+    if (n_shards < 1 || n_shards > DLLM_MAX_SHARDS)
+        return fail(DLLM_ERR_ARG, "dllm_step_decide_shards: n_shards=%d outside [1, %d]", n_shards, DLLM_MAX_SHARDS);
+    dllm_status rc = check_shape("dllm_step_decide_shards", DLLM_FP32, rows, L, V, nullptr, P);
+    if (rc == DLLM_OK)
+        rc = check_decide("dllm_step_decide_shards", input_ids, W, mask_in, mask_out, threshold, 0, p, b, conf, argmax,
+                          done, accept_len, status, P);
+    if (rc != DLLM_OK || rows == 0) return rc;
+    if (!triples) return fail(DLLM_ERR_ARG, "dllm_step_decide_shards: null triples");
+    P.partials = (float4 *)triples;            // the shards play the part of a slot's chunks
+    P.NC = n_shards;
+    return launch_decide(P, (hipStream_t)stream, kRuleThreshold);
 }

@@ -36,6 +36,8 @@ struct StepParams {
     const int32_t *p, *b;                     // never NULL here (see check_fit)
     int32_t check_fit;                        // p and b were given: check p + (b+1)L <= W
     int32_t S;                                // quota rule: diffusion steps per block (0: threshold rule)
+    float4 *triples;                          // vocabulary shards: [rows*L*n_shards] per-shard results
+    int32_t shard, n_shards, vocab_offset;    // this shard, the shard count, its first global column
     float *conf_out;
     int32_t *arg_out;
     uint8_t *done;
@@ -270,6 +272,9 @@ inline bool shape_of(int32_t rows, int32_t L, int32_t V, dllm_dtype dt, int &NV,
 
 // Launchers (score.hip, decide.hip): enqueue the kernels for checked parameters.
 dllm_status launch_score(const StepParams &P, dllm_dtype dtype, hipStream_t st);
-dllm_status launch_decide(const StepParams &P, hipStream_t st);
+// mode: kRuleThreshold / kRuleQuota apply the row's rule; kEmitTriples writes each masked slot's
+// merged (max, sum, global index) into P.triples at shard P.shard instead.
+constexpr int kRuleThreshold = 0, kRuleQuota = 1, kEmitTriples = 2;
+dllm_status launch_decide(const StepParams &P, hipStream_t st, int mode);
 
 }  // namespace dllm

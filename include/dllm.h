@@ -45,6 +45,7 @@ typedef enum { DLLM_FP32 = 0, DLLM_BF16 = 1 } dllm_dtype;
 #define DLLM_MAX_ROWS 4096         /* rows of a box / row capacity */
 #define DLLM_MAX_POSITIONS 262144  /* rows * L */
 #define DLLM_MAX_QUEUE 8192        /* queue capacity */
+#define DLLM_MAX_SHARDS 1024       /* vocabulary shards */
 
 /* Request table, indexed by request id ([BlockServe] §II-A: prompt length p_i, K_i = ceil(g_i/L)
  * blocks, current block index b_i).  All arrays are device memory of length n_req (blk_mask:
@@ -173,6 +174,36 @@ dllm_status dllm_step_decide_quota(void *stream, dllm_dtype dtype, int32_t rows,
                                    int32_t steps_per_block, const int32_t *p, const int32_t *b, float *conf,
                                    int32_t *argmax, uint8_t *done, int32_t *accept_len, void *workspace,
                                    size_t workspace_bytes, int32_t *status);
+
+/* dllm_step_score_shard and dllm_step_decide_shards — the step over a vocabulary split into
+ * n_shards contiguous column ranges (a tensor-parallel language-model head: [DiLaServe] §三 3.2 ②
+ * and §四 4.5 serve every step on tensor-parallel instances).
+ *
+ * dllm_step_score_shard scores shard `shard` (columns vocab_offset .. vocab_offset + V_shard - 1)
+ * of every masked slot: logits point at that shard's column 0 with the given strides (as for
+ * dllm_step, with V = V_shard).  For each masked slot it writes one record {float m, float S,
+ * int32 a, int32 0} = (max of the shard, sum of exp(x - m) over the shard, global index of the
+ * shard's first max) to triples[(r*L + j)*n_shards + shard]; other records are untouched.  The
+ * workspace is that of dllm_step for V_shard.
+ * dllm_step_decide_shards combines the n_shards records of every masked slot in shard order:
+ * m = max m_t, a = the smallest a_t with m_t = m, S = sum_t S_t exp(m_t - m), c = 1/S, by the fixed
+ * merge tree dllm_step uses for its chunks, and then applies the LowConfidence rule with the
+ * outputs and conditions of dllm_step (V = the whole vocabulary, for the argmax range check).
+ * Every rank of a tensor-parallel group that holds the same records reaches the same decisions.
+ * triples: device memory of dllm_shard_triples_bytes(rows, L, n_shards) bytes, 16-byte aligned.
+ * Errors: as dllm_step_score / dllm_step_decide, plus DLLM_ERR_ARG for a shard outside
+ * [0, n_shards), n_shards outside [1, DLLM_MAX_SHARDS], a negative vocab_offset or null triples. */
+size_t dllm_shard_triples_bytes(int32_t rows, int32_t L, int32_t n_shards);
+dllm_status dllm_step_score_shard(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+                                  int64_t row_stride, int32_t rows, int32_t L, int32_t V_shard,
+                                  int32_t vocab_offset, int32_t shard, int32_t n_shards,
+                                  const uint8_t *mask_in, void *workspace, size_t workspace_bytes,
+                                  void *triples, int32_t *status);
+dllm_status dllm_step_decide_shards(void *stream, int32_t n_shards, const void *triples, int32_t rows,
+                                    int32_t L, int32_t V, int32_t *input_ids, int32_t W,
+                                    const uint8_t *mask_in, uint8_t *mask_out, const float *threshold,
+                                    const int32_t *p, const int32_t *b, float *conf, int32_t *argmax,
+                                    uint8_t *done, int32_t *accept_len, int32_t *status);
 
 /* dllm_step_features — per-request inputs of a remaining-step predictor, after a step.
  *

@@ -147,6 +147,30 @@ def test_features_rejects_bad_arguments():
     assert call(rows=0, row_req=None, conf=None) == _lib.DLLM_OK
 
 
+def test_shards_reject_bad_arguments():
+    L = _lib.lib()
+    assert L.dllm_shard_triples_bytes(4, 32, 8) == 4 * 32 * 8 * 16
+    assert L.dllm_shard_triples_bytes(4, 32, 0) == 0
+    need = L.dllm_step_workspace_bytes(4, 32, 1000, 1)
+    f, ws = FAKE, ctypes.c_void_p(0x10000)
+
+    def sc(shard=0, n=2, off=0, tri=f, V=1000):
+        return L.dllm_step_score_shard(None, f, 1, V, 32 * V, 4, 32, V, off, shard, n, f, ws, need, tri, f)
+
+    def dc(n=2, tri=f, W=40):
+        return L.dllm_step_decide_shards(None, n, tri, 4, 32, 2000, f, W, f, ctypes.c_void_p(0x2000), f, None, None,
+                                         None, None, f, f, f)
+    assert sc(shard=2) == _lib.DLLM_ERR_ARG
+    assert sc(shard=-1) == _lib.DLLM_ERR_ARG
+    assert sc(n=0) == _lib.DLLM_ERR_ARG
+    assert sc(off=-5) == _lib.DLLM_ERR_ARG
+    assert sc(tri=None) == _lib.DLLM_ERR_ARG
+    assert dc(n=0) == _lib.DLLM_ERR_ARG
+    assert dc(n=2000) == _lib.DLLM_ERR_ARG
+    assert dc(tri=None) == _lib.DLLM_ERR_ARG
+    assert dc(W=31) == _lib.DLLM_ERR_SHAPE
+
+
 def test_step_rows_zero_is_noop():
     assert _step(rows=0, logits=None, ids=None) == _lib.DLLM_OK
 

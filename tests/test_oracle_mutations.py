@@ -19,6 +19,7 @@ PACK = "tests/test_oracle_pack_compact.py"
 LOOP = "tests/test_oracle_loop.py"
 QUOTA = "tests/test_oracle_quota.py"
 FEAT = "tests/test_oracle_features.py"
+SHARD = "tests/test_oracle_shard.py"
 
 MUTATIONS = [
     ("oracle/step.py", "S = float(np.sum(np.exp(x - m)))", "S = float(np.sum(np.exp(m - x)))", STEP),
@@ -48,6 +49,9 @@ MUTATIONS = [
     ("oracle/features.py", "f[2] = (b * L + unmasked) / (K * L)", "f[2] = ((b + 1) * L + unmasked) / (K * L)", FEAT),
     ("oracle/features.py", "f[5], f[6], f[8] = np.quantile(c, [0.25, 0.5, 0.75])",
      "f[5], f[6], f[8] = np.quantile(c, [0.25, 0.5, 0.75], method='lower')", FEAT),
+    ("oracle/shard.py", "a = min(t[1] for t in triples if t[0] == m)", "a = max(t[1] for t in triples if t[0] == m)",
+     SHARD),
+    ("oracle/shard.py", "S = sum(t[2] * np.exp(t[0] - m) for t in triples)", "S = sum(t[2] for t in triples)", SHARD),
 ]
 
 
@@ -67,7 +71,7 @@ def _run_pins(dst, pin_file):
 
 def test_unmodified_copy_passes(tmp_path):
     _copy_tree(str(tmp_path))
-    for pin in (STEP, PACK, LOOP, QUOTA, FEAT):
+    for pin in (STEP, PACK, LOOP, QUOTA, FEAT, SHARD):
         r = _run_pins(str(tmp_path), pin)
         assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
 
