@@ -315,6 +315,35 @@ def run_gpu(args):
     }
 
 
+def run_loop(cfg, mode):
+    """A whole loop of one configuration on the GPU (forward = the synthetic generator on the
+    device), with its accounting: batch steps, request-steps, idle request-steps (rows stepped
+    after their block finished), scheduler rounds and masked positions scored."""
+    import torch
+
+    from confidence_block_unmasking_amd.driver import Session
+    from workload import configs, synth
+    w = configs.make(cfg)
+    mode = mode or w.mode
+    if mode == "single":
+        raise SystemExit(f"configuration {cfg} is a single step, not a loop")
+
+    def fwd(sess):
+        synth.logits_gpu(sess.logits, w.dtype, sess.rows, w.L, w.V, sess.row_req, sess.b_rows,
+                         sess.masks[sess.cur], w.logit_seed, w.sigma, w.umax)
+    sess = Session.from_workload(w)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    st = sess.run(mode, fwd)
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    keys = ("steps", "request_steps", "idle_request_steps", "rounds", "positions_scored", "evicted", "admitted",
+            "max_cost")
+    return {"loop": w.name, "config": cfg, "mode": mode, "seconds": sec,
+            "masked_positions_per_s": st["positions_scored"] / sec, **{k: st[k] for k in keys},
+            "note": "wall time includes the synthetic forward (logits generation) of every step"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,6 +355,10 @@ def main():
                     help="unmasking rule: LowConfidence threshold (default) or the fixed per-step quota")
     ap.add_argument("--steps-per-block", type=int, default=32, help="diffusion steps per block (quota rule)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--loop", type=int, default=0, metavar="CONFIG",
+                    help="instead of the step benchmark, run the whole loop of configuration 2, 4 or 5")
+    ap.add_argument("--mode", choices=("sync", "fdfo", "handback"), default=None,
+                    help="loop mode for --loop (default: the configuration's own)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -342,6 +375,9 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.loop:
+        print(json.dumps(run_loop(args.loop, args.mode)), flush=True)
         return
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)   # before the GPU is touched
     out = run_gpu(args)

@@ -61,8 +61,8 @@ class Session:
         self.features_buf = torch.empty(n * api.N_FEATURES, dtype=f32, device=device)
         self.logits = logits if logits is not None else torch.empty((n, self.L, self.V), dtype=dtype, device=device)
         self.W = 0
-        self.stats = dict(steps=0, positions_scored=0, compacts=0, packs=0, idle_request_steps=0, max_cost=0,
-                          evicted=0, admitted=0)
+        self.stats = dict(steps=0, request_steps=0, positions_scored=0, compacts=0, packs=0, rounds=0,
+                          idle_request_steps=0, max_cost=0, evicted=0, admitted=0)
         self.step_events = []          # (start, end) cuda events of each dllm_step, when timing
 
     @classmethod
@@ -131,10 +131,13 @@ class Session:
     def run(self, mode, forward, max_steps=10**7, on_step=None, timed=False):
         """Drive compact -> pack -> (forward, step)* -> compact ... until queue and rows are empty.
 
-        forward(session) fills session.logits for the current box.  on_step(session, info) is
-        called after every step with the host copies (done, new mask) — the test harness uses it
-        to check each step.  Returns self.stats."""
-        assert mode in ("sync", "fdfo")
+        mode: "sync" (the batch runs until every block is done), "fdfo" (first-done-first-out with
+        the in-place re-loop: the batch is re-stepped as it stands until some block finishes) or
+        "handback" (first-done-first-out that hands control back to the scheduler after every step,
+        the behaviour the in-place re-loop removes).  forward(session) fills session.logits for the
+        current box.  on_step(session, info) is called after every step with the host copies (done,
+        new mask) — the test harness uses it to check each step.  Returns self.stats."""
+        assert mode in ("sync", "fdfo", "handback")
         self.compact(with_box=False)                 # admission at the start of the run
         while self.rows > 0:
             self.pack()
@@ -143,6 +146,7 @@ class Session:
                 if self.stats["steps"] >= max_steps:
                     raise RuntimeError("step limit reached")
                 masked_rows = (mask_host != 0).any(axis=1)
+                self.stats["request_steps"] += self.rows
                 self.stats["idle_request_steps"] += int((~masked_rows).sum())
                 self.stats["positions_scored"] += int((mask_host != 0).sum())
                 forward(self)
@@ -157,6 +161,9 @@ class Session:
                     break
                 if mode == "sync" and done.all():
                     break
+                if mode == "handback":
+                    break
+            self.stats["rounds"] += 1
             self.compact(with_box=True)
         return self.stats
 

@@ -13,6 +13,9 @@ From [FDFO] (page "FDFO: è®© dLLM æŽ¨ç†ä»Žã€Œæ•´æ‰¹ç­‰æœ€æ…¢ã€å˜æˆã€Œè°å…ˆå
   * Â§å·¥ç¨‹è®¾è®¡ä¸‰: the two modes are an execution switch, orthogonal to the unmasking algorithm.
 Reading: admission runs once at the start and after every hand-back to the scheduler
 (FDFO: a step with at least one done row; sync: a step with every row done).
+A third mode, "handback", is first-done-first-out without the in-place re-loop: control returns to
+the scheduler (scatter, admission, re-pack) after every step, which is what Â§å·¥ç¨‹è®¾è®¡å›› removes by
+keeping unfinished blocks in their slots; it produces the same tokens in more scheduler rounds.
 """
 from __future__ import annotations
 
@@ -29,11 +32,12 @@ def run(st: dict, rows: int, L: int, mask_id: int, pad_id: int, dtype: str, budg
 
     st: request table (see compact()); rows: number of active rows on entry.
     logits_fn(row_req, b_rows, mask_rows) -> logits [rows, L, V] for the current box.
-    Returns a trace dict: steps, idle_request_steps (rows stepped with no masked slot left),
-    positions_scored, and per-layout metas.
+    Returns a trace dict: steps (batch steps), request_steps (rows stepped, summed over steps),
+    idle_request_steps (rows stepped with no masked slot left), rounds (hand-backs to the scheduler
+    after steps), positions_scored, and per-layout metas.
     """
-    assert mode in ("sync", "fdfo")
-    trace = dict(steps=0, idle_request_steps=0, positions_scored=0, metas=[], max_cost=0)
+    assert mode in ("sync", "fdfo", "handback")
+    trace = dict(steps=0, request_steps=0, idle_request_steps=0, rounds=0, positions_scored=0, metas=[], max_cost=0)
     meta = compact(st, rows, L, 0, mask_id, eos_id, budget, rows_cap)
     trace["metas"].append(meta)
     rows, W = meta["rows"], meta["W"]
@@ -45,6 +49,7 @@ def run(st: dict, rows: int, L: int, mask_id: int, pad_id: int, dtype: str, budg
         while True:
             if trace["steps"] >= max_steps:
                 raise RuntimeError("step limit reached")
+            trace["request_steps"] += rows
             trace["idle_request_steps"] += int(np.sum(~(msk != 0).any(axis=1)))
             trace["positions_scored"] += int(np.sum(msk != 0))
             logits = logits_fn(st["row_req"][:rows].copy(), pk["b"], msk)
@@ -55,6 +60,9 @@ def run(st: dict, rows: int, L: int, mask_id: int, pad_id: int, dtype: str, budg
                 break
             if mode == "sync" and out["done"].all():
                 break
+            if mode == "handback":
+                break
+        trace["rounds"] += 1
         meta = compact(st, rows, L, W, mask_id, eos_id, budget, rows_cap, box_ids=ids, mask=msk,
                        done=out["done"])
         trace["metas"].append(meta)

@@ -236,3 +236,64 @@ def test_loop_config4_fdfo():
 def test_loop_config5_fdfo():
     lockstep_run(configs.config5(), full_score_max=0, sample=2, whole_rows=0, deep_every=25, label="c5",
                  features_every=25)
+
+
+def _abc_session(T, L=8, V=16):
+    """Three requests whose blocks need exactly T_i steps: T_i masked slots and constant logits
+    (confidence 1/V never clears the 0.9 threshold, so each step unmasks one slot)."""
+    from confidence_block_unmasking_amd.driver import Session
+    n = len(T)
+    p = np.full(n, 2, np.int32)
+    off = np.arange(n, dtype=np.int64) * (2 + L)
+    arena = np.full(n * (2 + L), -5, np.int32)
+    blk_mask = np.zeros((n, L), np.uint8)
+    for q, t in enumerate(T):
+        blk_mask[q, :t] = 1
+        arena[off[q] + 2 + t:off[q] + 2 + L] = 3
+    return Session(p, np.ones(n, np.int32), np.zeros(n, np.int32), np.ones(n, np.int32), np.full(n, 0.9, np.float32),
+                   off, arena, blk_mask, np.arange(n, dtype=np.int32), n, np.zeros(0, np.int32), L=L, V=V,
+                   dtype=torch.float32, rows_cap=n, mask_id=-5, pad_id=-6)
+
+
+def test_loop_abc_accounting_sync_fdfo_handback():
+    """The A/B/C example of the FDFO page on the GPU: idle request-steps, request-steps and
+    scheduler rounds of the three loop modes."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "abc_idle.json")))
+    T = [g["T"]["A"], g["T"]["B"], g["T"]["C"]]
+    for mode in ("sync", "fdfo", "handback"):
+        sess = _abc_session(T)
+        stats = sess.run(mode, lambda s: s.logits.zero_())
+        assert stats["steps"] == max(T), mode
+        assert stats["idle_request_steps"] == g[f"{mode}_idle_request_steps"], mode
+        assert stats["request_steps"] == g[f"{mode}_request_steps"], mode
+        assert stats["rounds"] == g[f"{mode}_rounds"], mode
+        h = sess.host_table()
+        assert np.all(h["state"] == configs.FINISHED)
+
+
+def test_loop_modes_same_tokens_and_oracle_traces():
+    """Sync, FDFO and hand-back runs on the GPU give every request the same tokens, and each run's
+    accounting equals the oracle loop's for the same mode."""
+    from confidence_block_unmasking_amd.driver import Session
+    w = configs.small(L=4, V=64, n_act=0, n_q=9, K=3, seed=41, dtype="fp32", rows_cap=4, p_range=(1, 6))
+    w.row_req = np.full(4, -1, np.int32)
+    fwd = gpu_forward(w)
+    arenas = {}
+    for mode in ("sync", "fdfo", "handback"):
+        sess = Session.from_workload(w)
+        stats = sess.run(mode, fwd)
+        arenas[mode] = sess.host_table()["arena"]
+        st = _oracle_state(w)
+
+        def fn(row_req, b_rows, mask_rows):
+            return synth.logits_cpu(len(row_req), w.L, w.V, w.dtype, row_req, b_rows, mask_rows, w.logit_seed,
+                                    w.sigma, w.umax)
+        tr = oloop.run(st, 0, w.L, w.mask_id, w.pad_id, w.dtype, w.budget, w.rows_cap, mode, fn)
+        if np.array_equal(arenas[mode], st["arena"]):     # no decision forked on a near-tie
+            for k in ("steps", "request_steps", "idle_request_steps", "rounds", "positions_scored"):
+                assert stats[k] == tr[k], (mode, k, stats[k], tr[k])
+        print(f"{mode}: {dict((k, stats[k]) for k in ('steps', 'request_steps', 'idle_request_steps', 'rounds'))}",
+              flush=True)
+    assert np.array_equal(arenas["sync"], arenas["fdfo"]) and np.array_equal(arenas["fdfo"], arenas["handback"])

@@ -40,9 +40,16 @@ def test_abc_idle_request_steps_sync_vs_fdfo():
     tr = oloop.run(st, 3, L, -5, -6, "fp32", 0, 3, "sync", const_logits)
     assert tr["steps"] == g["sync_steps"]
     assert tr["idle_request_steps"] == g["sync_idle_request_steps"]
+    assert tr["request_steps"] == g["sync_request_steps"] and tr["rounds"] == g["sync_rounds"]
     st, L, V = _abc_state(T)
     tr = oloop.run(st, 3, L, -5, -6, "fp32", 0, 3, "fdfo", const_logits)
     assert tr["idle_request_steps"] == g["fdfo_idle_request_steps"]
+    assert tr["steps"] == max(T)
+    assert tr["request_steps"] == g["fdfo_request_steps"] and tr["rounds"] == g["fdfo_rounds"]
+    st, L, V = _abc_state(T)
+    tr = oloop.run(st, 3, L, -5, -6, "fp32", 0, 3, "handback", const_logits)
+    assert tr["idle_request_steps"] == g["handback_idle_request_steps"]
+    assert tr["request_steps"] == g["handback_request_steps"] and tr["rounds"] == g["handback_rounds"]
     assert tr["steps"] == max(T)
 
 
@@ -73,7 +80,8 @@ def test_schedule_invariance_bs1_sync_fdfo(seed):
     any row capacity or budget: the logits are keyed by the request's own state."""
     w = configs.small(L=4, V=48, n_act=0, n_q=7, K=3, seed=seed, dtype="bf16", sigma=1, umax=6)
     results = []
-    for mode, cap, budget in [("sync", 7, 0), ("fdfo", 7, 0), ("fdfo", 2, 0), ("fdfo", 7, 30), ("sync", 3, 0)]:
+    for mode, cap, budget in [("sync", 7, 0), ("fdfo", 7, 0), ("fdfo", 2, 0), ("fdfo", 7, 30), ("sync", 3, 0),
+                              ("handback", 7, 0), ("handback", 2, 30)]:
         st = _state(w)
         st["row_req"] = np.full(w.n_req, -1, np.int64)
         tr = oloop.run(st, 0, w.L, w.mask_id, w.pad_id, w.dtype, budget, cap, mode, _gen(w))
@@ -107,3 +115,4 @@ def test_fdfo_never_slower_in_steps_than_sync_for_one_batch():
     assert steps["fdfo"]["idle_request_steps"] == 0
     assert steps["sync"]["positions_scored"] == steps["fdfo"]["positions_scored"]
     assert steps["sync"]["steps"] == steps["fdfo"]["steps"]
+    assert steps["fdfo"]["request_steps"] <= steps["sync"]["request_steps"]

@@ -41,6 +41,7 @@ MUTATIONS = [
     ("oracle/compact.py", "slots = sorted(freed) + list(range(rows, rows_cap))",
      "slots = list(range(rows, rows_cap)) + sorted(freed)", PACK),
     ("oracle/loop.py", 'if mode == "sync" and out["done"].all():', 'if mode == "sync" and out["done"].any():', LOOP),
+    ("oracle/loop.py", 'trace["request_steps"] += rows', 'trace["request_steps"] += 1', LOOP),
     ("oracle/quota.py", "return [base + (1 if t < rem else 0) for t in range(S)]",
      "return [base + (1 if t >= S - rem else 0) for t in range(S)]", QUOTA),
     ("oracle/quota.py", "js.sort(key=lambda j: (-float(conf[j]), j))", "js.sort(key=lambda j: (-float(conf[j]), -j))",
