@@ -242,6 +242,18 @@ def run_gpu(args):
         decide_args = (stream, _lib.DLLM_BF16, rows, L, V, P(box), W, P(mask_a), P(mask_b), P(sess.tau),
                        P(sess.p_rows), P(sess.b_rows), P(sess.conf), P(sess.argmax), P(sess.done), P(sess.accept), ws,
                        wsn, P(sess.status))
+    if args.shards > 1:
+        # vocabulary split into args.shards contiguous slices, scored one after the other (what each
+        # rank of a tensor-parallel group would do with its own slice), then combined and decided
+        pts = [V * t // args.shards for t in range(args.shards + 1)]
+        tri = torch.zeros(rows * L * args.shards * 16, dtype=torch.uint8, device="cuda")
+        shard_args = [[(stream, vp(bufs[k].data_ptr() + 2 * pts[t]), _lib.DLLM_BF16, V, L * V, rows, L,
+                        pts[t + 1] - pts[t], pts[t], t, args.shards, P(mask_a), ws, wsn, P(tri), P(sess.status))
+                       for t in range(args.shards)] for k in range(args.rotate)]
+        decide_fn = lib.dllm_step_decide_shards
+        decide_args = (stream, args.shards, P(tri), rows, L, V, P(box), W, P(mask_a), P(mask_b),
+                       P(sess.tau), P(sess.p_rows), P(sess.b_rows), P(sess.conf), P(sess.argmax), P(sess.done),
+                       P(sess.accept), P(sess.status))
     pack_args, comp_args = [], []
     for c in copies:
         pack_args.append((stream, rows, L, W, w.pad_id, P(c.row_req), ctypes.byref(c.reqs), P(box),
@@ -261,9 +273,17 @@ def run_gpu(args):
         e = ev.get(k)
         if e:
             e[0].record()
-        rc |= lib.dllm_step_score(*score_args[k % args.rotate])
-        if e:
-            e[1].record()
+        if args.shards > 1:
+            sa = shard_args[k % args.rotate]
+            rc |= lib.dllm_step_score_shard(*sa[0])
+            if e:
+                e[1].record()
+            for t in range(1, args.shards):
+                rc |= lib.dllm_step_score_shard(*sa[t])
+        else:
+            rc |= lib.dllm_step_score(*score_args[k % args.rotate])
+            if e:
+                e[1].record()
         rc |= decide_fn(*decide_args)
         rc |= lib.dllm_compact(*comp_args[k])
         return rc
@@ -286,7 +306,8 @@ def run_gpu(args):
     kern_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(args.warmup, n_total) if k in ev])
     kern_s = float(kern_ms.mean()) / 1e3
     step_bytes = M * V * 2
-    achieved = step_bytes / kern_s / 1e9
+    timed_bytes = step_bytes if args.shards <= 1 else M * (V // args.shards) * 2
+    achieved = timed_bytes / kern_s / 1e9
     return {
         "metric": METRIC,
         "value": M * args.steps / elapsed,
@@ -304,6 +325,7 @@ def run_gpu(args):
                                "thresholds {0.5..0.9}, masked fraction U[0.1,1.0]; step = pack + score + decide + "
                                "compact",
                    "rule": "threshold" if args.rule == "threshold" else f"quota, {args.steps_per_block} steps per block",
+                   "vocab_shards": max(1, args.shards),
                    "requests": w.rows, "block_len": L, "vocab": V, "logits_dtype": "bf16",
                    "masked_positions_per_step": M, "box_width": W, "logits_buffers": args.rotate},
         "logits_GBps": step_bytes * args.steps / elapsed / 1e9,
@@ -311,7 +333,10 @@ def run_gpu(args):
                             "p50": float(np.percentile(kern_ms, 50)) * 1e3,
                             "p90": float(np.percentile(kern_ms, 90)) * 1e3},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": stored_traffic(M)},
+                     "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": stored_traffic(M) if args.shards <= 1 and args.rule == "threshold" else None},
+        **({"timed_kernel": f"dllm_step_score_shard of shard 0 of {args.shards} (scoring + per-slot shard record)"}
+           if args.shards > 1 else {}),
     }
 
 
@@ -354,6 +379,7 @@ def main():
     ap.add_argument("--rule", choices=("threshold", "quota"), default="threshold",
                     help="unmasking rule: LowConfidence threshold (default) or the fixed per-step quota")
     ap.add_argument("--steps-per-block", type=int, default=32, help="diffusion steps per block (quota rule)")
+    ap.add_argument("--shards", type=int, default=1, help="score the vocabulary in this many slices and combine")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--loop", type=int, default=0, metavar="CONFIG",
                     help="instead of the step benchmark, run the whole loop of configuration 2, 4 or 5")
