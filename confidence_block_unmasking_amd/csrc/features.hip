@@ -19,6 +19,9 @@ using namespace dllm;
 constexpr int kThreads = 256;
 constexpr int kFeatures = 9;
 
+// NaN stored as its bit pattern (the library is built without NaN semantics in arithmetic).
+__device__ __forceinline__ void store_nan(float *p) { *(uint32_t *)p = 0x7FC00000u; }
+
 __device__ double quantile(const float *sorted, int n, double q) {
     const double pos = q * (n - 1);
     const int lo = (int)floor(pos);
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void features_kernel(int32_t L, const int
     const int q = row_req[row];
     if (q < 0 || q >= R.n_req || R.K[q] < 1) {
         set_status(status, DLLM_ERR_ARG);
-        for (int k = 0; k < kFeatures; ++k) f[k] = __builtin_nanf("");
+        for (int k = 0; k < kFeatures; ++k) store_nan(f + k);
         return;
     }
     const int K = R.K[q], b = R.b[q], n = s_n;
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void features_kernel(int32_t L, const int
     f[2] = (float)(((double)b * L + unmasked) / ((double)K * L));
     f[3] = (float)((double)unmasked / L);
     if (n == 0) {
-        for (int k = 4; k < kFeatures; ++k) f[k] = __builtin_nanf("");
+        for (int k = 4; k < kFeatures; ++k) store_nan(f + k);
         return;
     }
     double sum = 0.0;
