@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(StepParams P, int win) 
     int pk_v = 0, pk_at = 0;
     int nbuf = 0;
     int q = uni(t / NC), c = t - q * NC;
-    const char *rowp = P.logits + s_off[q - q_lo];
+    const char *rowp = P.logits + uni64(s_off[q - q_lo]);
     int slot = uni(s_id[q - q_lo]);
     u32x4 raw[kVPL];
     if (ALIGNED) issue(raw, rowp, c * kCH, min(kCH, P.NV - c * kCH));
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(StepParams P, int win) 
             qn = uni(tn / NC);
             cn = tn - qn * NC;
             if (qn != q) {
-                rowp = P.logits + s_off[qn - q_lo];
+                rowp = P.logits + uni64(s_off[qn - q_lo]);
                 slot = uni(s_id[qn - q_lo]);
             }
             if (ALIGNED) issue(raw, rowp, cn * kCH, min(kCH, P.NV - cn * kCH));

@@ -47,6 +47,12 @@ struct StepParams {
 };
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// A wave-uniform 64-bit value moved to scalar registers, so that addresses built from it stay scalar.
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // ---- wave reductions: DPP within each row of 16 lanes, then the four rows through readlane ----
 // A fixed network, so the result's bits do not depend on timing; every lane gets the result.
@@ -77,6 +83,33 @@ __device__ __forceinline__ float red_sum(float v) {
     v += dppf<kHalfMirror>(v);
     v += dppf<kRowMirror>(v);
     return (rlf(v, 0) + rlf(v, 16)) + (rlf(v, 32) + rlf(v, 48));
+}
+// The same reductions with the four rows combined by DPP row broadcasts (lane 15 of a row into the
+// next row, then lane 31 into rows 2 and 3): lane 63 ends with the result, read once.  Rows that
+// a broadcast does not write keep the identity element as their operand.
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dppf_rows(float idle, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(idle), __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float red_max_bc(float v) {
+    v = fmaxf(v, dppf<kQuadSwap1>(v));
+    v = fmaxf(v, dppf<kQuadSwap2>(v));
+    v = fmaxf(v, dppf<kHalfMirror>(v));
+    v = fmaxf(v, dppf<kRowMirror>(v));
+    v = fmaxf(v, dppf_rows<kRowBcast15, 0xA>(-INFINITY, v));
+    v = fmaxf(v, dppf_rows<kRowBcast31, 0xC>(-INFINITY, v));
+    return rlf(v, 63);
+}
+__device__ __forceinline__ float red_sum_bc(float v) {
+    v += dppf<kQuadSwap1>(v);
+    v += dppf<kQuadSwap2>(v);
+    v += dppf<kHalfMirror>(v);
+    v += dppf<kRowMirror>(v);
+    v += dppf_rows<kRowBcast15, 0xA>(0.0f, v);
+    v += dppf_rows<kRowBcast31, 0xC>(0.0f, v);
+    return rlf(v, 63);
 }
 __device__ __forceinline__ int red_min(int v) {
     v = min(v, dppi<kQuadSwap1>(v));
@@ -132,22 +165,25 @@ struct Part {
 };
 
 // Chunk reduction over values already in registers: x[k][e] is element (vb + k*64 + lane)*E + e
-// of the row; -inf marks padding.  Lane-local max and sum exp(x - max), then the wave combine.
-// The lowest vector holding the max comes from a DPP min; its owner lane and slot k are then
-// wave-uniform, so that one vector's E values are read with readlane and the first element equal
-// to the max gives the exact index without going back to memory.
+// of the row; -inf marks padding.  Per-vector maxima, the lane max, the lane sum of exp(x - max),
+// then the wave combine.  The lowest vector holding the wave max is found from one ballot per
+// vector slot k (vector index k*64 + lane grows with k first, then lane); its owner lane and k are
+// wave-uniform, so that vector's E values are read with readlane and the first element equal to
+// the max gives the exact index without going back to memory.  A chunk whose values are all -inf
+// reports no index.
 template <int E>
 __device__ __forceinline__ Part reduce_lanes(float (&x)[kVPL][E], int vb) {
-    const int lane = lane_id();
-    float m = -INFINITY;
-    int kb = -1;
+    float vm[kVPL];
 #pragma unroll
     for (int k = 0; k < kVPL; ++k) {
-        float vm = x[k][0];
+        float a = x[k][0];
 #pragma unroll
-        for (int e = 1; e < E; ++e) vm = fmaxf(vm, x[k][e]);
-        if (vm > m) { m = vm; kb = k; }
+        for (int e = 1; e < E; ++e) a = fmaxf(a, x[k][e]);
+        vm[k] = a;
     }
+    float m = vm[0];
+#pragma unroll
+    for (int k = 1; k < kVPL; ++k) m = fmaxf(m, vm[k]);
     const float nml = (m == -INFINITY) ? 0.0f : -m * kLog2e;
     float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
@@ -159,13 +195,20 @@ __device__ __forceinline__ Part reduce_lanes(float (&x)[kVPL][E], int vb) {
         }
     }
     Part r;
-    r.m = red_max(m);
+    r.m = red_max_bc(m);
     const float scale = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m - r.m) * kLog2e);
-    r.s = red_sum((s0 + s1) * scale);
-    const int vmin = red_min((kb >= 0 && m == r.m) ? kb * 64 + lane : 0x7FFFFFFF);   // chunk-relative
+    r.s = red_sum_bc((s0 + s1) * scale);
     int elem = 0x7FFFFFFF;
-    if (vmin != 0x7FFFFFFF) {
-        const int kw = vmin >> 6, lw = vmin & 63;                   // wave-uniform
+    if (r.m != -INFINITY) {
+        int kw = 0, lw = 0;
+#pragma unroll
+        for (int k = kVPL - 1; k >= 0; --k) {
+            const uint64_t bal = __ballot(vm[k] == r.m);
+            if (bal != 0) {
+                kw = k;
+                lw = __builtin_ctzll(bal);
+            }
+        }
         int ef = E;
 #pragma unroll
         for (int k = 0; k < kVPL; ++k) {
@@ -175,7 +218,7 @@ __device__ __forceinline__ Part reduce_lanes(float (&x)[kVPL][E], int vb) {
                     if (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[k][e]), lw)) == r.m) ef = e;
             }
         }
-        elem = (vb + vmin) * E + ef;
+        elem = (vb + kw * 64 + lw) * E + ef;
     }
     r.v = elem;
     return r;
@@ -195,15 +238,18 @@ __device__ __forceinline__ void issue(u32x4 (&raw)[kVPL], const char *row, int v
         for (int k = 0; k < kVPL; ++k) raw[k] = __builtin_nontemporal_load(base + min(k * 64 + lane, n - 1));
     }
 }
+// n is wave-uniform: full chunks take no masking work at all, only a row's short last chunk does.
 template <bool BF16>
 __device__ __forceinline__ void convert(const u32x4 (&raw)[kVPL], float (&x)[kVPL][Fmt<BF16>::E], int n) {
-    const int lane = lane_id();
 #pragma unroll
-    for (int k = 0; k < kVPL; ++k) {
-        unpack<BF16>(raw[k], x[k]);
-        if (n < kCH && k * 64 + lane >= n) {
+    for (int k = 0; k < kVPL; ++k) unpack<BF16>(raw[k], x[k]);
+    if (n < kCH) {
+        const int lane = lane_id();
 #pragma unroll
-            for (int e = 0; e < Fmt<BF16>::E; ++e) x[k][e] = -INFINITY;
+        for (int k = 0; k < kVPL; ++k) {
+            const bool pad = k * 64 + lane >= n;
+#pragma unroll
+            for (int e = 0; e < Fmt<BF16>::E; ++e) x[k][e] = pad ? -INFINITY : x[k][e];
         }
     }
 }
