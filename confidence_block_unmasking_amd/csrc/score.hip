@@ -28,8 +28,7 @@ namespace dllm {
 // Kernel 1: score every chunk of every masked slot.
 template <bool BF16, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void score_kernel(StepParams P, int win) {
-    extern __shared__ int64_t s_off[];         // [win] byte offset of the window's logits rows
-    int *s_id = (int *)(s_off + win);          // [win] slot index (row*L + j) of the same
+    extern __shared__ int s_id[];              // [win] slot index (row*L + j) of the window's masked slots
     __shared__ int s_tmp[2][kWaves];
     __shared__ int s_next;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -64,22 +63,17 @@ __global__ __launch_bounds__(kThreads) void score_kernel(StepParams P, int win) 
     const int t0 = g * per + min(g, rem), t1 = t0 + per + (g < rem ? 1 : 0);
     if (t0 >= t1) return;                      // uniform over the workgroup
     const int q_lo = t0 / NC, q_hi = (t1 - 1) / NC;
-    // list masked numbers q_lo..q_hi; qq = masked number of the first masked slot among mb's 16
+    // list the slots of masked numbers q_lo..q_hi; qq = masked number of the first masked slot
+    // among mb's 16, which start at slot s0.  Only the slot index is stored: the row address is
+    // formed later in scalar registers (the 64-bit multiplies would cost the listing wave about
+    // 0.1 us per entry here).
     auto extract = [&](uint32_t mb, int qq, int s0) {
         const int c = __popc(mb);
         if (c == 0 || qq > q_hi || qq + c <= q_lo) return;
         for (; qq < q_lo; ++qq) mb &= mb - 1;
-        int r = s0 / L, jb = s0 - r * L;
-        int prev = 0;
-        while (mb != 0 && qq <= q_hi) {
-            const int bit = __builtin_ctz(mb);
+        for (; mb != 0 && qq <= q_hi; ++qq) {
+            s_id[qq - q_lo] = s0 + __builtin_ctz(mb);
             mb &= mb - 1;
-            jb += bit - prev;
-            prev = bit;
-            while (jb >= L) { jb -= L; ++r; }
-            s_off[qq - q_lo] = (int64_t)r * P.row_stride_b + (int64_t)jb * P.pos_stride_b;
-            s_id[qq - q_lo] = r * L + jb;
-            ++qq;
         }
     };
     extract(mb0, off0 + incl0 - c0, tid * 16);
@@ -113,9 +107,14 @@ __global__ __launch_bounds__(kThreads) void score_kernel(StepParams P, int win) 
     float pk_m = 0.0f, pk_s = 0.0f;
     int pk_v = 0, pk_at = 0;
     int nbuf = 0;
+    // first byte of slot s's logits row (s wave-uniform: scalar arithmetic)
+    auto row_of = [&](int s) -> const char * {
+        const int r = s / L, j = s - r * L;
+        return P.logits + (int64_t)r * P.row_stride_b + (int64_t)j * P.pos_stride_b;
+    };
     int q = uni(t / NC), c = t - q * NC;
-    const char *rowp = P.logits + uni64(s_off[q - q_lo]);
     int slot = uni(s_id[q - q_lo]);
+    const char *rowp = row_of(slot);
     u32x4 raw[kVPL];
     if (ALIGNED) issue(raw, rowp, c * kCH, min(kCH, P.NV - c * kCH));
     while (true) {
@@ -135,8 +134,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(StepParams P, int win) 
             qn = uni(tn / NC);
             cn = tn - qn * NC;
             if (qn != q) {
-                rowp = P.logits + uni64(s_off[qn - q_lo]);
                 slot = uni(s_id[qn - q_lo]);
+                rowp = row_of(slot);
             }
             if (ALIGNED) issue(raw, rowp, cn * kCH, min(kCH, P.NV - cn * kCH));
         }
@@ -166,7 +165,7 @@ dllm_status launch_score(const StepParams &P, dllm_dtype dtype, hipStream_t st) 
     const bool aligned = ((uintptr_t)P.logits & 15) == 0 && (P.pos_stride_b & 15) == 0 &&
                          (P.row_stride_b & 15) == 0 && (P.V % (16 / es)) == 0;
     // grid: one workgroup per compute unit; more when the LDS window of masked slots would
-    // exceed 2048 entries (24 KiB of dynamic LDS); fewer when a fully masked box has fewer chunks
+    // exceed 2048 entries (8 KiB of dynamic LDS); fewer when a fully masked box has fewer chunks
     // than that many waves
     int64_t grid = cu_count();
     if (grid < (S + 2047) / 2048) grid = (S + 2047) / 2048;
@@ -176,7 +175,7 @@ dllm_status launch_score(const StepParams &P, dllm_dtype dtype, hipStream_t st) 
     // window: masked slots touched by one workgroup's ceil(M*NC/grid) chunks, for M <= S
     const int64_t per = (S * NC + grid - 1) / grid;
     const int win = (int)((per + NC - 1) / NC + 2);
-    const size_t lds = (size_t)win * (sizeof(int64_t) + sizeof(int));
+    const size_t lds = (size_t)win * sizeof(int);
     if (dtype == DLLM_BF16) {
         if (aligned) hipLaunchKernelGGL((score_kernel<true, true>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
         else hipLaunchKernelGGL((score_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
