@@ -22,39 +22,65 @@ __device__ __forceinline__ void set_status(int32_t *status, int32_t code) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+// ---- whole-wave operations (every lane active) on DPP: no LDS round trip ----------------------
+// Rows of 16 lanes first (quad swaps and mirrors for reductions, right shifts for the scan), then
+// the four rows joined by row broadcasts (lane 15 of a row into the next row, lane 31 into rows 2
+// and 3); a reduction's result is read from lane 63, so every lane gets it.
+namespace wave_dpp {
+constexpr int kQuad1 = 0xB1, kQuad2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118;
+constexpr int kBcast15 = 0x142, kBcast31 = 0x143;
+// lane i reads lane CTRL(i); rows outside ROWS, and (with BC) lanes whose source lies outside the
+// row, read `idle`
+template <int CTRL, int ROWS = 0xF, bool BC = false>
+__device__ __forceinline__ int mov(int idle, int v) {
+    return __builtin_amdgcn_update_dpp(idle, v, CTRL, ROWS, 0xF, BC);
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float movf(float idle, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(idle), __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+}  // namespace wave_dpp
+
+__device__ __forceinline__ float wave_max(float v) {
+    using namespace wave_dpp;
+    v = fmaxf(v, movf<kQuad1>(v, v));
+    v = fmaxf(v, movf<kQuad2>(v, v));
+    v = fmaxf(v, movf<kHalfMirror>(v, v));
+    v = fmaxf(v, movf<kMirror>(v, v));
+    v = fmaxf(v, movf<kBcast15, 0xA>(-INFINITY, v));
+    v = fmaxf(v, movf<kBcast31, 0xC>(-INFINITY, v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i(int v, int identity, Op op) {
+    using namespace wave_dpp;
+    v = op(v, mov<kQuad1>(v, v));
+    v = op(v, mov<kQuad2>(v, v));
+    v = op(v, mov<kHalfMirror>(v, v));
+    v = op(v, mov<kMirror>(v, v));
+    v = op(v, mov<kBcast15, 0xA>(identity, v));
+    v = op(v, mov<kBcast31, 0xC>(identity, v));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 __device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-    return v;
+    return wave_reduce_i(v, 0x7FFFFFFF, [](int a, int b) { return min(a, b); });
 }
 __device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-    return v;
+    return wave_reduce_i(v, (int)0x80000000, [](int a, int b) { return max(a, b); });
 }
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    return wave_reduce_i(v, 0, [](int a, int b) { return a + b; });
 }
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int t = __shfl_up(v, o, 64);
-        if (lane >= o) v += t;
-    }
+    using namespace wave_dpp;
+    v += mov<kShr1, 0xF, true>(0, v);
+    v += mov<kShr2, 0xF, true>(0, v);
+    v += mov<kShr4, 0xF, true>(0, v);
+    v += mov<kShr8, 0xF, true>(0, v);
+    v += mov<kBcast15, 0xA>(0, v);
+    v += mov<kBcast31, 0xC>(0, v);
     return v;
 }
 

@@ -121,23 +121,41 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
     if (MODE == kEmitTriples) return;
     __syncthreads();
     int nmasked = 0;
+    bool u_lane = false;                       // quota rule, L <= 64: wave 0 lane j's slot unmasks
     if (QUOTA) {
-        // every thread: the masked count and k; then the rank of each of its masked slots among the
-        // row's masked slots by (confidence descending, slot ascending); rank < k unmasks
-        for (int g = 0; g < L; g += 64) nmasked += __popcll(__ballot(g + lane < L && s_mask[g + lane]));
-        const int k = quota_for_remaining(L, P.S, nmasked);
-        for (int j = tid; j < L; j += kDecideThreads) {
-            bool u = false;
-            if (s_mask[j]) {
-                const float cj = s_conf[j];
-                int rank = 0;
-                for (int i = 0; i < L; ++i)
-                    rank += s_mask[i] && (s_conf[i] > cj || (s_conf[i] == cj && i < j));
-                u = rank < k;
+        // the masked count and k; then the rank of each masked slot among the row's masked slots
+        // by (confidence descending, slot ascending); rank < k unmasks
+        if (L <= 64) {
+            // one slot per lane of wave 0, the others read from registers
+            if (wave != 0) return;
+            const bool mj = lane < L && s_mask[lane] != 0;
+            const float cj = mj ? s_conf[lane] : 0.0f;
+            const uint64_t mb = __ballot(mj);
+            nmasked = __popcll(mb);
+            const int k = quota_for_remaining(L, P.S, nmasked);
+            int rank = 0;
+            for (int i = 0; i < L; ++i) {
+                const float ci = rlf(cj, i);
+                rank += ((mb >> i) & 1) && (ci > cj || (ci == cj && i < lane));
             }
-            s_u[j] = u;
+            u_lane = mj && rank < k;
+        } else {
+            for (int g = 0; g < L; g += 64) nmasked += __popcll(__ballot(g + lane < L && s_mask[g + lane]));
+            const int k = quota_for_remaining(L, P.S, nmasked);
+            for (int j = tid; j < L; j += kDecideThreads) {
+                bool u = false;
+                if (s_mask[j]) {
+                    const float cj = s_conf[j];
+                    int rank = 0;
+#pragma unroll 8
+                    for (int i = 0; i < L; ++i)
+                        rank += s_mask[i] && (s_conf[i] > cj || (s_conf[i] == cj && i < j));
+                    u = rank < k;
+                }
+                s_u[j] = u;
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
     if (wave != 0) return;
     const float tau = __int_as_float(__builtin_amdgcn_readlane(rule_in, 0));
@@ -165,7 +183,7 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
     for (int g = 0; g < L; g += 64) {
         const int j = g + lane;
         const bool masked = j < L && s_mask[j];
-        const bool u = masked && (QUOTA ? s_u[j] != 0 : any_above ? (s_conf[j] > tau) : (j == best_j));
+        const bool u = masked && (QUOTA ? (L <= 64 ? u_lane : s_u[j] != 0) : any_above ? (s_conf[j] > tau) : (j == best_j));
         n_unmasked += __popcll(__ballot(u));
         if (j < L) {
             const int64_t qi = (int64_t)row * L + j;

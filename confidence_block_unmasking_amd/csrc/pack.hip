@@ -7,7 +7,7 @@
 //   §II-E 向量化混合调度执行: gather of each request's active block into the batch.
 //
 // One workgroup per row; lanes stride over the W columns with coalesced 4-byte stores.  Integer
-// gather only; bound by the O(rows * W) bytes it writes (a few MB at the largest shapes).
+// gather only: O(rows * W) bytes written (a few MB at the largest shapes).
 #include "common.h"
 
 namespace {
@@ -16,6 +16,11 @@ using namespace dllm;
 
 constexpr int kThreads = 256;
 
+constexpr int kUnroll = 8;   // box columns per thread whose loads go out together
+
+// Latency-bound (a few kilobytes per row): three dependent memory round trips per row, the row's
+// request id, then every field of that request at once, then the arena gather and the block mask,
+// each thread issuing all its loads before any of its stores.
 __global__ __launch_bounds__(kThreads) void pack_kernel(int32_t L, int32_t W, int32_t pad_id,
                                                         const int32_t *__restrict__ row_req, dllm_reqs R,
                                                         int32_t *__restrict__ box_ids, uint8_t *__restrict__ box_valid,
@@ -24,29 +29,62 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(int32_t L, int32_t W, in
                                                         int32_t *__restrict__ b_out, int32_t *status) {
     const int r = blockIdx.x;
     const int q = row_req[r];
-    const bool ok_id = q >= 0 && q < R.n_req && R.state[q] == 1 && R.b[q] >= 0 && R.b[q] < R.K[q];
-    int64_t w = 0, pad = W, off = 0;
-    if (ok_id) {
-        w = (int64_t)R.p[q] + ((int64_t)R.b[q] + 1) * L;
+    const bool in_range = q >= 0 && q < R.n_req;
+    int st = 0, bq = -1, Kq = 0, pq = 0;
+    int64_t off = 0;
+    float th = 0.0f;
+    if (in_range) {                            // one branch: the six loads go out together
+        st = R.state[q];
+        bq = R.b[q];
+        Kq = R.K[q];
+        pq = R.p[q];
         off = R.arena_off[q];
-        pad = W - w;
+        th = R.threshold[q];
     }
+    const bool ok_id = in_range && st == 1 && bq >= 0 && bq < Kq;
+    int64_t pad = W;
+    if (ok_id) pad = W - ((int64_t)pq + ((int64_t)bq + 1) * L);
     const bool fits = ok_id && pad >= 0;
     if (threadIdx.x == 0) {
         if (!ok_id) set_status(status, DLLM_ERR_ARG);
         else if (!fits) set_status(status, DLLM_ERR_SHAPE);
-        tau[r] = ok_id ? R.threshold[q] : 0.0f;
-        p_out[r] = ok_id ? R.p[q] : 0;
-        b_out[r] = ok_id ? R.b[q] : 0;
+        tau[r] = ok_id ? th : 0.0f;
+        p_out[r] = ok_id ? pq : 0;
+        b_out[r] = ok_id ? bq : 0;
+    }
+    // the block mask (L <= 4 * kThreads) and the first kUnroll strides of columns: loads first
+    uint8_t mv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = threadIdx.x + u * kThreads;
+        mv[u] = 0;
+        if (ok_id && j < L) mv[u] = R.blk_mask[(int64_t)q * L + j];
     }
     const int64_t rb = (int64_t)r * W;
-    for (int c = threadIdx.x; c < W; c += kThreads) {
-        const bool valid = fits && c >= pad;
-        box_ids[rb + c] = valid ? R.arena[off + (c - pad)] : pad_id;
-        if (box_valid) box_valid[rb + c] = valid ? 1 : 0;
-        if (box_pos) box_pos[rb + c] = valid ? (int32_t)(c - pad) : 0;
+    for (int c0 = threadIdx.x; c0 < W; c0 += kUnroll * kThreads) {
+        int v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int c = c0 + u * kThreads;
+            v[u] = pad_id;
+            if (fits && c < W && c >= pad) v[u] = R.arena[off + (c - pad)];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int c = c0 + u * kThreads;
+            if (c < W) {
+                const bool valid = fits && c >= pad;
+                box_ids[rb + c] = v[u];
+                if (box_valid) box_valid[rb + c] = valid ? 1 : 0;
+                if (box_pos) box_pos[rb + c] = valid ? (int32_t)(c - pad) : 0;
+            }
+        }
     }
-    for (int j = threadIdx.x; j < L; j += kThreads) mask[(int64_t)r * L + j] = ok_id ? R.blk_mask[(int64_t)q * L + j] : 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = threadIdx.x + u * kThreads;
+        if (j < L) mask[(int64_t)r * L + j] = mv[u];
+    }
 }
 
 }  // namespace
