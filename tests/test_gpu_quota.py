@@ -57,7 +57,7 @@ def check_quota_step(logits, dtype, ids, mask, S, g):
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("rows,L,V,S", [(4, 32, 1024, 32), (3, 32, 5000, 10), (5, 64, 2051, 32), (2, 7, 300, 3),
-                                        (6, 100, 777, 200)])
+                                        (6, 100, 777, 200), (2, 1024, 130, 32)])
 def test_quota_parity_random(dtype, rows, L, V, S):
     rng = np.random.default_rng(rows * 100 + L + S)
     logits, ids, mask, _ = _rand_case(rng, rows, L, V, dtype, p_mask=0.7)
@@ -71,7 +71,7 @@ def test_quota_parity_random(dtype, rows, L, V, S):
         assert np.array_equal(g[k], h[k]), k
 
 
-@pytest.mark.parametrize("L,S", [(32, 32), (32, 10), (7, 3), (64, 32), (5, 8), (40, 1)])
+@pytest.mark.parametrize("L,S", [(32, 32), (32, 10), (7, 3), (64, 32), (5, 8), (40, 1), (65, 9), (100, 7)])
 def test_quota_count_for_every_masked_count(L, S):
     # row m has m masked slots: it unmasks exactly quota_for_remaining(L, S, m)
     rng = np.random.default_rng(L * 7 + S)

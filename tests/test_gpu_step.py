@@ -149,7 +149,7 @@ def _rand_case(rng, rows, L, V, dtype, p_mask=0.5, W_extra=3, scale=2.0, planted
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("rows,L,V", [(1, 1, 1), (3, 5, 7), (2, 32, 1000), (2, 32, 1001), (4, 64, 4099),
-                                      (2, 100, 515), (1, 7, 65536), (5, 33, 8200)])
+                                      (2, 100, 515), (1, 7, 65536), (5, 33, 8200), (2, 1024, 300)])
 def test_step_shapes_and_ragged_tails(dtype, rows, L, V):
     rng = np.random.default_rng(rows * 1000 + L * 10 + V)
     logits, ids, mask, tau = _rand_case(rng, rows, L, V, dtype)
