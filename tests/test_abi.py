@@ -227,3 +227,10 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         _lib.lib()
+
+
+def test_binding_limits_match_the_header():
+    text = open(os.path.join(ROOT, "include", "dllm.h")).read()
+    got = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define DLLM_(MAX_\w+)\s+(\d+)", text)}
+    assert got["MAX_L"] == _lib.MAX_L and got["MAX_ROWS"] == _lib.MAX_ROWS
+    assert got["MAX_POSITIONS"] == _lib.MAX_POSITIONS and got["MAX_QUEUE"] == _lib.MAX_QUEUE

@@ -182,6 +182,16 @@ def test_pack_compact_parity_random_small():
         lockstep_run(w, full_score_max=10**9, label=f"small{seed}")
 
 
+def test_loop_at_the_row_limit():
+    """Every row of a DLLM_MAX_ROWS-row box active, then a refill from the queue: step, pack and
+    compact against the oracle at the largest box the library accepts."""
+    from confidence_block_unmasking_amd import _lib
+    cap = _lib.MAX_ROWS
+    w = configs.small(L=2, V=16, n_act=cap, n_q=48, K=1, seed=41, dtype="fp32", rows_cap=cap, p_range=(1, 6))
+    res = lockstep_run(w, full_score_max=10**9, label="maxrows")
+    assert res["steps"] >= 2
+
+
 def test_loop_end_of_sequence_evicts_early():
     """With an end-of-sequence id, requests whose committed block holds it leave before block K."""
     w = configs.small(L=4, V=16, n_act=0, n_q=10, K=4, seed=32, dtype="fp32", rows_cap=4, p_range=(1, 8))

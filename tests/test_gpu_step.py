@@ -184,6 +184,19 @@ def test_step_many_slots(rows, L, V, dtype, p_mask, moff):
     check_step(logits, dtype, ids, mask, tau, g)
 
 
+def test_step_at_the_position_limit():
+    # rows * L = DLLM_MAX_POSITIONS slots in one call (rows = DLLM_MAX_ROWS)
+    from confidence_block_unmasking_amd import _lib
+    rows = _lib.MAX_ROWS
+    L = _lib.MAX_POSITIONS // rows
+    rng = np.random.default_rng(5)
+    logits, ids, mask, tau = _rand_case(rng, rows, L, 8, "bf16", p_mask=0.5)
+    print(f"position limit rows={rows} L={L}", flush=True)
+    g = gpu_step(logits, "bf16", ids, mask, tau)
+    assert g["status"] == 0
+    check_step(logits, "bf16", ids, mask, tau, g)
+
+
 def test_step_halves_equal_step():
     # dllm_step_score then dllm_step_decide gives dllm_step's outputs bit for bit
     from confidence_block_unmasking_amd import api
