@@ -40,6 +40,15 @@ __global__ __launch_bounds__(kThreads) void score_kernel(StepParams P, int win) 
     //    LDS, those whose chunks fall in this workgroup's share.  Thread tid covers slots
     //    tid*16 .. tid*16+15 of each tile of kTile slots.
     const uint32_t mb0 = mask_bits16(P.mask_in, tid * 16, S);
+    // The launch values used after the scan, fetched while the mask load is in flight (left to
+    // themselves they are loaded at first use, a dependent round trip in the middle of the prologue).
+    {
+        const int G0 = gridDim.x, NV0 = P.NV;
+        const char *lg0 = P.logits;
+        const int64_t rs0 = P.row_stride_b, ps0 = P.pos_stride_b;
+        const float4 *pa0 = P.partials;
+        asm volatile("" ::"s"(G0), "s"(NC), "s"(NV0), "s"(lg0), "s"(rs0), "s"(ps0), "s"(pa0));
+    }
     int c0 = __popc(mb0);
     const int incl0 = wave_incl_scan(c0);
     if (lane == 63) s_tmp[0][wave] = incl0;

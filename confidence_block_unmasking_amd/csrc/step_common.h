@@ -47,12 +47,6 @@ struct StepParams {
 };
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-// A wave-uniform 64-bit value moved to scalar registers, so that addresses built from it stay scalar.
-__device__ __forceinline__ int64_t uni64(int64_t v) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
 
 // ---- wave reductions: DPP within each row of 16 lanes, then the four rows through readlane ----
 // A fixed network, so the result's bits do not depend on timing; every lane gets the result.
