@@ -22,6 +22,18 @@ __device__ __forceinline__ void set_status(int32_t *status, int32_t code) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// Device: make the listed kernel-argument values available at this point.  Their scalar loads
+// then go out together at the start instead of each at its first use, where every wait would be
+// one more dependent round trip in a latency-bound kernel.
+template <typename T>
+__device__ __forceinline__ void fetch_arg(const T &v) {
+    asm volatile("" ::"s"(v));
+}
+template <typename... T>
+__device__ __forceinline__ void fetch_args(const T &...v) {
+    (fetch_arg(v), ...);
+}
+
 // ---- whole-wave operations (every lane active) on DPP: no LDS round trip ----------------------
 // Rows of 16 lanes first (quad swaps and mirrors for reductions, right shifts for the scan), then
 // the four rows joined by row broadcasts (lane 15 of a row into the next row, lane 31 into rows 2

@@ -70,8 +70,11 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactParams P) {
 
     // 1. every load that does not depend on another one: queue length, the rows' request ids and
     //    done flags, the queue ids (up to its capacity); then the request fields they point to
+    fetch_args(P.rows, P.L, P.W, P.mask_id, P.eos_id, P.rows_cap, P.box_ids, P.mask, P.done, P.row_req, R.n_req, R.p,
+               R.K, R.b, R.state, R.arena_off, R.arena, R.blk_mask, P.q_ids, P.q_len, P.q_cap, P.budget, P.meta,
+               P.status);
     int qlen_raw = 0;
-    if (tid == 0) qlen_raw = *P.q_len;
+    if (tid == 0) qlen_raw = __builtin_nontemporal_load(P.q_len);   // a vector load: no wait until used
     int rq[kRowsPerThread], rdone[kRowsPerThread];
 #pragma unroll
     for (int k = 0; k < kRowsPerThread; ++k) {

@@ -54,6 +54,8 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
     int *s_arg = (int *)(s_conf + L);           // [L]
     uint8_t *s_mask = (uint8_t *)(s_arg + L);   // [L]
     uint8_t *s_u = s_mask + L;                  // [L] quota rule: slot unmasked this step
+    fetch_args(P.mask_in, P.partials, P.tau, P.p, P.b, P.ids, P.mask_out, P.conf_out, P.arg_out, P.done, P.accept,
+               P.W, P.V, P.check_fit, P.status);
     const uint8_t *mrow = P.mask_in + (int64_t)row * L;
     const float4 *prow = P.partials + (int64_t)row * L * NC;
     // inputs of the rule first (lanes 0, 1, 2: tau, p, b; one vector load), so that their

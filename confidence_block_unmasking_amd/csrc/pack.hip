@@ -27,6 +27,8 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(int32_t L, int32_t W, in
                                                         int32_t *__restrict__ box_pos, uint8_t *__restrict__ mask,
                                                         float *__restrict__ tau, int32_t *__restrict__ p_out,
                                                         int32_t *__restrict__ b_out, int32_t *status) {
+    fetch_args(row_req, R.n_req, R.p, R.K, R.b, R.state, R.threshold, R.arena_off, R.arena, R.blk_mask, box_ids,
+               box_valid, box_pos, mask, tau, p_out, b_out, status, L, W, pad_id);
     const int r = blockIdx.x;
     const int q = row_req[r];
     const bool in_range = q >= 0 && q < R.n_req;
