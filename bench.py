@@ -391,8 +391,8 @@ def main():
                     help="write the traffic file from four rocprofv3 --pmc CSV output folders (no GPU use)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); rows of the step "
-              "shard across GPUs without any exchange, but no multi-GPU path is built", file=sys.stderr)
+        print(f"bench.py: the step runs on one GPU only (asked for --gpus {args.gpus}); its rows would shard "
+              "across GPUs without any exchange, but no multi-GPU launcher is provided", file=sys.stderr)
         sys.exit(2)
     if args.record_traffic:
         from workload import configs
