@@ -74,7 +74,7 @@ def cpu_baseline(cpu_seconds):
 
     from oracle import pack as opack
     from workload import configs, synth
-    w = configs.config3()
+    w = configs.dream_step()
     W = opack.box_width(w.row_req, w.rows, w.p, w.b, w.L)
     pk = opack.pack(w.row_req, w.rows, w.L, W, w.pad_id, w.p, w.b, w.threshold, w.arena_off, w.arena, w.blk_mask)
     _CPU.update(logits=synth.logits_cpu(w.rows, w.L, w.V, w.dtype, w.row_req, pk["b"], pk["mask"], w.logit_seed,
@@ -204,7 +204,7 @@ def run_gpu(args):
     from confidence_block_unmasking_amd.driver import Session
     from workload import configs, synth
 
-    w = configs.config3()
+    w = configs.dream_step()
     sess = Session.from_workload(w)
     L, V = w.L, w.V
     sess.compact(with_box=False)                       # initial layout: rows and box width
@@ -340,18 +340,18 @@ def run_gpu(args):
     }
 
 
-def run_loop(cfg, mode):
-    """A whole loop of one configuration on the GPU (forward = the synthetic generator on the
+def run_loop(name, mode):
+    """A whole loop of one workload on the GPU (forward = the synthetic generator on the
     device), with its accounting: batch steps, request-steps, idle request-steps (rows stepped
     after their block finished), scheduler rounds and masked positions scored."""
     import torch
 
     from confidence_block_unmasking_amd.driver import Session
     from workload import configs, synth
-    w = configs.make(cfg)
+    w = configs.make(name)
     mode = mode or w.mode
     if mode == "single":
-        raise SystemExit(f"configuration {cfg} is a single step, not a loop")
+        raise SystemExit(f"{name} is a single step, not a loop")
 
     def fwd(sess):
         synth.logits_gpu(sess.logits, w.dtype, sess.rows, w.L, w.V, sess.row_req, sess.b_rows,
@@ -364,7 +364,7 @@ def run_loop(cfg, mode):
     sec = time.perf_counter() - t0
     keys = ("steps", "request_steps", "idle_request_steps", "rounds", "positions_scored", "evicted", "admitted",
             "max_cost")
-    return {"loop": w.name, "config": cfg, "mode": mode, "seconds": sec,
+    return {"loop": w.name, "mode": mode, "seconds": sec,
             "masked_positions_per_s": st["positions_scored"] / sec, **{k: st[k] for k in keys},
             "note": "wall time includes the synthetic forward (logits generation) of every step"}
 
@@ -381,10 +381,10 @@ def main():
     ap.add_argument("--steps-per-block", type=int, default=32, help="diffusion steps per block (quota rule)")
     ap.add_argument("--shards", type=int, default=1, help="score the vocabulary in this many slices and combine")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--loop", type=int, default=0, metavar="CONFIG",
-                    help="instead of the step benchmark, run the whole loop of configuration 2, 4 or 5")
+    ap.add_argument("--loop", default=None, metavar="WORKLOAD",
+                    help="instead of the step benchmark, run a whole loop: llada-sync, blockserve-mixed or large-fdfo")
     ap.add_argument("--mode", choices=("sync", "fdfo", "handback"), default=None,
-                    help="loop mode for --loop (default: the configuration's own)")
+                    help="loop mode for --loop (default: the workload's own)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -396,13 +396,16 @@ def main():
         sys.exit(2)
     if args.record_traffic:
         from workload import configs
-        w = configs.config3()
+        w = configs.dream_step()
         record_traffic(*args.record_traffic, masked=int(w.blk_mask[w.row_req[:w.rows]].sum()))
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
     if args.loop:
+        from workload import configs
+        if args.loop not in configs.LOOPS:
+            raise SystemExit(f"--loop takes one of {', '.join(configs.LOOPS)}")
         print(json.dumps(run_loop(args.loop, args.mode)), flush=True)
         return
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)   # before the GPU is touched

@@ -228,23 +228,23 @@ def test_compact_capacity_error_on_gpu():
     assert api.read_meta(sess.meta)["rows"] == 0
 
 
-def test_loop_config1_sync():
-    w = configs.config1()
+def test_loop_tiny_step_sync():
+    w = configs.tiny_step()
     w.mode = "sync"
-    lockstep_run(w, full_score_max=10**9, label="c1")
+    lockstep_run(w, full_score_max=10**9, label="tiny")
 
 
-def test_loop_config2_sync():
-    lockstep_run(configs.config2(), full_score_max=32, sample=32, whole_rows=1, label="c2")
+def test_loop_llada_sync():
+    lockstep_run(configs.llada_sync(), full_score_max=32, sample=32, whole_rows=1, label="llada")
 
 
-def test_loop_config4_fdfo():
-    lockstep_run(configs.config4(), full_score_max=0, sample=4, whole_rows=0, deep_every=5, label="c4",
+def test_loop_blockserve_mixed_fdfo():
+    lockstep_run(configs.blockserve_mixed(), full_score_max=0, sample=4, whole_rows=0, deep_every=5, label="blockserve",
                  features_every=10)
 
 
-def test_loop_config5_fdfo():
-    lockstep_run(configs.config5(), full_score_max=0, sample=2, whole_rows=0, deep_every=25, label="c5",
+def test_loop_large_fdfo():
+    lockstep_run(configs.large_fdfo(), full_score_max=0, sample=2, whole_rows=0, deep_every=25, label="large",
                  features_every=25)
 
 

@@ -96,22 +96,22 @@ def _packed_step_inputs(w):
     return pk, logits
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
-def test_step_parity_configs(cfg):
-    w = configs.make(cfg)
+@pytest.mark.parametrize("name", ["tiny-step", "llada-sync", "dream-dynamic-step"])
+def test_step_parity_workloads(name):
+    w = configs.make(name)
     pk, logits = _packed_step_inputs(w)
-    print(f"config {cfg}: rows={w.rows} L={w.L} V={w.V} masked={int(pk['mask'].sum())}", flush=True)
+    print(f"{name}: rows={w.rows} L={w.L} V={w.V} masked={int(pk['mask'].sum())}", flush=True)
     g = gpu_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"], pk["p"], pk["b"])
     assert g["status"] == 0
     err, n_amb = check_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"], g, pk["p"], pk["b"])
-    print(f"config {cfg}: max conf error {err:.3g}, ambiguous rows {n_amb}")
+    print(f"{name}: max conf error {err:.3g}, ambiguous rows {n_amb}")
     assert np.array_equal(g["ids"][:, :-w.L], pk["box_ids"][:, :-w.L])        # prompt columns untouched
 
 
 def test_generator_gpu_matches_cpu():
     from confidence_block_unmasking_amd import api  # noqa: F401
-    for cfg in (1, 3):
-        w = configs.make(cfg)
+    for name in ("tiny-step", "dream-dynamic-step"):
+        w = configs.make(name)
         rows = min(w.rows, 8)
         rr = w.row_req[:rows]
         blk = w.b[rr].astype(np.int32)
@@ -200,7 +200,7 @@ def test_step_at_the_position_limit():
 def test_step_halves_equal_step():
     # dllm_step_score then dllm_step_decide gives dllm_step's outputs bit for bit
     from confidence_block_unmasking_amd import api
-    w = configs.config3()
+    w = configs.dream_step()
     pk, logits = _packed_step_inputs(w)
     a = gpu_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"])
     rows, L, V = logits.shape
@@ -228,7 +228,7 @@ def test_step_halves_equal_step():
 
 def test_step_in_place_mask_update():
     # mask_out = mask_in: the same results as with two buffers
-    w = configs.config3()
+    w = configs.dream_step()
     pk, logits = _packed_step_inputs(w)
     a = gpu_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"])
     b = gpu_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"], in_place=True)
@@ -280,7 +280,7 @@ def test_step_many_chunks_merge_path():
 
 
 def test_step_never_reads_unmasked_slots():
-    w = configs.config1()
+    w = configs.tiny_step()
     pk, logits = _packed_step_inputs(w)           # unmasked slots hold NaN
     assert np.isnan(logits[pk["mask"] == 0]).all()
     g = gpu_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"])
@@ -297,7 +297,7 @@ def test_step_status_for_row_that_does_not_fit():
 
 
 def test_step_determinism_and_batch_invariance():
-    w = configs.config3()
+    w = configs.dream_step()
     pk, logits = _packed_step_inputs(w)
     a = gpu_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"])
     b = gpu_step(logits, w.dtype, pk["box_ids"], pk["mask"], pk["threshold"])

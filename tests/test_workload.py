@@ -53,7 +53,7 @@ def test_generator_bf16_is_rne_of_fp32():
 
 
 def test_logits_fill_masked_only_with_nan_elsewhere():
-    w = configs.config1()
+    w = configs.tiny_step()
     lg = synth.logits_cpu(w.rows, w.L, w.V, w.dtype, w.row_req, w.b[w.row_req[:w.rows]],
                           w.blk_mask[w.row_req[:w.rows]], w.logit_seed, w.sigma, w.umax)
     m = w.blk_mask[w.row_req[:w.rows]] != 0
@@ -66,9 +66,9 @@ def test_logits_fill_masked_only_with_nan_elsewhere():
     assert np.array_equal(lg[r, j], one)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_config_shapes(cfg):
-    w = configs.make(cfg)
+@pytest.mark.parametrize("name", list(configs.WORKLOADS))
+def test_workload_shapes(name):
+    w = configs.make(name)
     assert w.arena.shape[0] == int((w.p.astype(np.int64) + w.K.astype(np.int64) * w.L).sum())
     act = w.row_req[:w.rows]
     assert np.all(w.state[act] == configs.ACTIVE)
@@ -80,14 +80,14 @@ def test_config_shapes(cfg):
         o = int(w.arena_off[q]) + int(w.p[q]) + int(w.b[q]) * w.L
         blk = w.arena[o:o + w.L]
         assert np.array_equal(blk == w.mask_id, w.blk_mask[q] == 1)
-    if cfg == 1:
+    if name == "tiny-step":
         assert w.rows == 4 and np.all(w.blk_mask.sum(1) == 16) and w.b.tolist() == [0, 1, 0, 1]
-    if cfg == 3:
+    if name == "dream-dynamic-step":
         mf = w.blk_mask.sum(1)
         assert mf.min() >= 1 and mf.max() <= 32 and 900 < mf.sum() < 1350
-    if cfg == 4:
+    if name == "blockserve-mixed":
         W = int((w.p[act] + (w.b[act] + 1) * w.L).max())
         assert w.rows * W <= w.budget
         assert np.all(w.K == 8)
-    if cfg == 5:
+    if name == "large-fdfo":
         assert w.rows == 0 and len(w.queue) == 2048 and w.K.min() >= 2 and w.K.max() <= 16

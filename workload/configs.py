@@ -1,4 +1,4 @@
-"""Seeded synthetic workloads for the five configurations (request-level draws only).
+"""Seeded synthetic workloads, five of them (request-level draws only).
 
 Input generation, shared by the GPU path's tests/bench and by the oracle's tests.  Nothing here
 computes any part of the unmasking method: it only draws prompt lengths, generation lengths,
@@ -10,7 +10,8 @@ Citation key for the shapes borrowed from the pages:
 Block length L = 32 and bf16 logits follow [BlockServe] §III-A; generation length 256 follows the
 output length of [DiLaServe] §五 setup; the threshold candidates {0.5,...,0.9} and the default 0.9
 follow [DiLaServe] §四 4.1 (paper §3.1).  Vocabulary sizes 126464 / 152064 are those of the
-LLaDA / Dream shaped configurations.  Every draw comes from numpy's default_rng(1000 + config).
+LLaDA / Dream shaped workloads.  Every draw comes from numpy's default_rng(seed) with a fixed seed per
+workload (1001 ... 1005).
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ TAU_SET = (0.5, 0.6, 0.7, 0.8, 0.9)
 @dataclasses.dataclass
 class Workload:
     name: str
-    cfg: int
+    seed_id: int        # fixed per workload: the draws use default_rng(1000 + seed_id)
     L: int
     V: int
     dtype: str          # "fp32" or "bf16"
@@ -64,7 +65,7 @@ class Workload:
                      if isinstance(getattr(self, f.name), np.ndarray)})
 
 
-def _build(name, cfg, L, V, dtype, sigma, umax, p, K, b, threshold, active, queue_ids, budget,
+def _build(name, seed_id, L, V, dtype, sigma, umax, p, K, b, threshold, active, queue_ids, budget,
            rows_cap, mode, masked_sets, rng):
     n = len(p)
     mask_id, pad_id = V, V + 1
@@ -96,14 +97,14 @@ def _build(name, cfg, L, V, dtype, sigma, umax, p, K, b, threshold, active, queu
     row_req = np.full(rows_cap, -1, np.int32)
     row_req[:len(active)] = active
     queue = np.array(sorted(queue_ids, key=lambda q: (int(p[q]), int(q))), np.int32)
-    return Workload(name=name, cfg=cfg, L=L, V=V, dtype=dtype, sigma=sigma, umax=umax,
-                    logit_seed=1000 + cfg, mask_id=mask_id, pad_id=pad_id, p=p, K=K, b=b,
+    return Workload(name=name, seed_id=seed_id, L=L, V=V, dtype=dtype, sigma=sigma, umax=umax,
+                    logit_seed=1000 + seed_id, mask_id=mask_id, pad_id=pad_id, p=p, K=K, b=b,
                     state=state, threshold=np.asarray(threshold, np.float32), arena_off=arena_off,
                     arena=arena, blk_mask=blk_mask, row_req=row_req, rows=len(active), queue=queue,
                     budget=int(budget), rows_cap=int(rows_cap), mode=mode)
 
 
-def config1() -> Workload:
+def tiny_step() -> Workload:
     """Tiny step: 4 requests, L=32, V=1024, fp32, sd 1, offset U[0,12]; p~U[8,32]; K=2, b_i = i mod 2;
     exactly 16 of 32 slots masked (seeded permutation); threshold 0.9."""
     rng = np.random.default_rng(1001)
@@ -114,7 +115,7 @@ def config1() -> Workload:
                   [0.9] * n, list(range(n)), [], 0, n, "single", ms, rng)
 
 
-def config2() -> Workload:
+def llada_sync() -> Workload:
     """LLaDA-shaped synchronous run: 32 requests, L=32, V=126464, bf16, sd 2, offset U[0,14];
     p~U[64,512]; one block each, fully masked; threshold 0.9; step until every block is done."""
     rng = np.random.default_rng(1002)
@@ -124,7 +125,7 @@ def config2() -> Workload:
                   list(range(n)), [], 0, n, "sync", [None] * n, rng)
 
 
-def config3() -> Workload:
+def dream_step() -> Workload:
     """Dream-shaped step with per-request thresholds: 64 requests, L=32, V=152064, bf16, sd 2,
     offset U[0,14]; p~U[64,512], b=0; threshold uniform over {0.5,...,0.9}; masked fraction
     f~U[0.1,1.0] per block -> max(1, floor(f*L + 0.5)) slots, the first of a seeded permutation."""
@@ -141,7 +142,7 @@ def config3() -> Workload:
                   list(range(n)), [], 0, n, "single", ms, rng)
 
 
-def config4() -> Workload:
+def blockserve_mixed() -> Workload:
     """BlockServe mixed-state run: 128 active requests with p~U[32,1024], g=256 (K=8), b~U{0..7},
     each at a fresh fully-masked block; 512 more queued with the same p law, sorted by (p, id);
     token budget 262144; threshold 0.9; V=126464 bf16, sd 2, offset U[0,14]; first-done-first-out."""
@@ -155,7 +156,7 @@ def config4() -> Workload:
                   list(range(n_act)), list(range(n_act, n)), 262144, n, "fdfo", [None] * n, rng)
 
 
-def config5() -> Workload:
+def large_fdfo() -> Workload:
     """Large first-done-first-out run: up to 256 rows, L=64, V=152064 bf16, sd 2, offset U[0,16];
     2048 queued requests, p~U[256,4096], g~U[128,1024] (K = ceil(g/64)), threshold uniform over
     {0.5,...,0.9}; starts empty; no token budget."""
@@ -169,11 +170,13 @@ def config5() -> Workload:
                   0, 256, "fdfo", [None] * n, rng)
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+WORKLOADS = {"tiny-step": tiny_step, "llada-sync": llada_sync, "dream-dynamic-step": dream_step,
+             "blockserve-mixed": blockserve_mixed, "large-fdfo": large_fdfo}
+LOOPS = ("llada-sync", "blockserve-mixed", "large-fdfo")   # the workloads that run as whole loops
 
 
-def make(cfg: int) -> Workload:
-    return CONFIGS[cfg]()
+def make(name: str) -> Workload:
+    return WORKLOADS[name]()
 
 
 def small(L=4, V=64, n_act=3, n_q=5, K=2, seed=7, dtype="fp32", budget=0, rows_cap=None,
