@@ -49,14 +49,24 @@ def new_workspace(rows: int, L: int, V: int, dtype=torch.bfloat16, device="cuda"
 
 
 def _logits_shape(logits, rows, L, V, pos_stride, row_stride):
+    """Shape and strides (in elements) of the logits; the kernels read element (r, j, v) at
+    r*row_stride + j*pos_stride + v, so the tensor's storage must reach that far."""
     if logits.dtype not in _DT:
         raise ValueError(f"logits dtype {logits.dtype} not supported")
+    if not logits.is_cuda:
+        raise ValueError("logits must be a device tensor")
     if rows is None:
         rows, L, V = logits.shape
     if pos_stride is None:
         pos_stride = logits.stride(1) if logits.dim() == 3 else V
     if row_stride is None:
         row_stride = logits.stride(0) if logits.dim() == 3 else L * pos_stride
+    if rows > 0 and L > 0 and V > 0:
+        reach = (rows - 1) * row_stride + (L - 1) * pos_stride + V
+        avail = logits.untyped_storage().nbytes() // logits.element_size() - logits.storage_offset()
+        if reach > avail:
+            raise ValueError(f"logits storage holds {avail} elements past its offset; rows={rows}, L={L}, V={V} "
+                             f"with strides ({row_stride}, {pos_stride}) reach {reach}")
     return rows, L, V, pos_stride, row_stride
 
 

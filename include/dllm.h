@@ -52,7 +52,10 @@ typedef enum { DLLM_FP32 = 0, DLLM_BF16 = 1 } dllm_dtype;
  * n_req * L bytes, row-major).  arena holds, for request q starting at arena_off[q], its
  * p[q] prompt tokens followed by K[q] blocks of L tokens (block k at arena_off[q] + p[q] + k*L);
  * blk_mask[q] is the mask of its current block (1 = masked): the half-finished block a request
- * carries between rounds ([FDFO] §工程设计二, dllm_incomplete_ids). */
+ * carries between rounds ([FDFO] §工程设计二, dllm_incomplete_ids).  The caller guarantees that
+ * every region lies inside the arena's allocation: the table carries no arena length, so the
+ * library cannot check it, and a region past the end makes dllm_pack and dllm_compact access
+ * memory outside the arena.  Ids, b and state are checked (DLLM_ERR_ARG in *status). */
 typedef struct {
     int32_t n_req;
     const int32_t *p;          /* prompt length */

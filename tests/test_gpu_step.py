@@ -197,6 +197,27 @@ def test_step_at_the_position_limit():
     check_step(logits, "bf16", ids, mask, tau, g)
 
 
+def test_binding_rejects_logits_smaller_than_the_shape():
+    # the C ABI cannot see a tensor's extent; the binding refuses shapes and strides that would
+    # read past the logits' storage, before anything is launched
+    from confidence_block_unmasking_amd import api
+    rows, L, V = 2, 4, 64
+    lg = torch.zeros(rows * L * V - 1, dtype=torch.bfloat16, device="cuda")
+    mask = torch.ones(rows * L, dtype=torch.uint8, device="cuda")
+    ws = api.new_workspace(rows, L, V, torch.bfloat16)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="reach"):
+        api.dllm_step_score(lg, mask, ws, st, rows=rows, L=L, V=V)
+    full = torch.zeros(rows * L * V + 8, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="reach"):
+        api.dllm_step_score(full[9:], mask, ws, st, rows=rows, L=L, V=V)
+    with pytest.raises(ValueError, match="reach"):
+        api.dllm_step_score(full, mask, ws, st, rows=rows, L=L, V=V, pos_stride=V + 2)
+    api.dllm_step_score(full[8:], mask, ws, st, rows=rows, L=L, V=V)   # exactly enough
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+
+
 def test_step_halves_equal_step():
     # dllm_step_score then dllm_step_decide gives dllm_step's outputs bit for bit
     from confidence_block_unmasking_amd import api
