@@ -254,8 +254,12 @@ def run_gpu(args):
         decide_args = (stream, args.shards, P(tri), rows, L, V, P(box), W, P(mask_a), P(mask_b),
                        P(sess.tau), P(sess.p_rows), P(sess.b_rows), P(sess.conf), P(sess.argmax), P(sess.done),
                        P(sess.accept), P(sess.status))
-    pack_args, comp_args = [], []
+    pack_args, comp_args, feat_args = [], [], []
+    feats = torch.empty(rows * 9, dtype=torch.float32, device="cuda")
     for c in copies:
+        # step-predictor features of the rows after the step (read before compact moves them)
+        feat_args.append((stream, rows, L, P(c.row_req), ctypes.byref(c.reqs), P(sess.conf), P(mask_b), P(feats),
+                          P(sess.status)))
         pack_args.append((stream, rows, L, W, w.pad_id, P(c.row_req), ctypes.byref(c.reqs), P(box),
                           P(sess.box_valid), P(sess.box_pos), P(mask_a), P(sess.tau), P(sess.p_rows), P(sess.b_rows),
                           P(sess.status)))
@@ -285,6 +289,8 @@ def run_gpu(args):
             if e:
                 e[1].record()
         rc |= decide_fn(*decide_args)
+        if args.features:
+            rc |= lib.dllm_step_features(*feat_args[k])
         rc |= lib.dllm_compact(*comp_args[k])
         return rc
 
@@ -326,6 +332,7 @@ def run_gpu(args):
                                "compact",
                    "rule": "threshold" if args.rule == "threshold" else f"quota, {args.steps_per_block} steps per block",
                    "vocab_shards": max(1, args.shards),
+                   **({"features": "dllm_step_features after each decision"} if args.features else {}),
                    "requests": w.rows, "block_len": L, "vocab": V, "logits_dtype": "bf16",
                    "masked_positions_per_step": M, "box_width": W, "logits_buffers": args.rotate},
         "logits_GBps": step_bytes * args.steps / elapsed / 1e9,
@@ -381,6 +388,8 @@ def main():
     ap.add_argument("--steps-per-block", type=int, default=32, help="diffusion steps per block (quota rule)")
     ap.add_argument("--shards", type=int, default=1, help="score the vocabulary in this many slices and combine")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--features", action="store_true",
+                    help="also compute the step-predictor features of every row after each step")
     ap.add_argument("--loop", default=None, metavar="WORKLOAD",
                     help="instead of the step benchmark, run a whole loop: llada-sync, blockserve-mixed or large-fdfo")
     ap.add_argument("--mode", choices=("sync", "fdfo", "handback"), default=None,

@@ -9,7 +9,8 @@
 //
 // One workgroup per row.  The confidences the step scored (conf >= 0) are ranked in LDS (ascending,
 // ties by slot), so thread 0 can interpolate the quantiles linearly between order statistics at
-// position q*(n-1) and sum them in order in double precision.  Latency-bound: kilobytes per row.
+// position q*(n-1) and sum them in order in double precision.  Latency-bound: kilobytes per row,
+// so the request lookup (two dependent loads) runs beside the confidence loads, not after them.
 #include "common.h"
 
 namespace {
@@ -37,19 +38,37 @@ __global__ __launch_bounds__(kThreads) void features_kernel(int32_t L, const int
     extern __shared__ float s_c[];             // [L] this row's confidences, -1 where not scored
     float *s_sorted = s_c + L;                 // [L] scored confidences in ascending order
     __shared__ int s_n, s_masked;
+    fetch_args(L, row_req, R.n_req, R.K, R.b, R.threshold, conf, mask_after, out, status);
     const int row = blockIdx.x, tid = threadIdx.x;
-    if (tid == 0) { s_n = 0; s_masked = 0; }
-    int nm = 0, ns = 0;
-    for (int j = tid; j < L; j += kThreads) {
-        const float c = conf[(int64_t)row * L + j];
-        s_c[j] = c;
-        ns += c >= 0.0f;
-        nm += mask_after[(int64_t)row * L + j] != 0;
+    // Two dependent loads (the row's request, then its fields) on thread 0, while waves 1.. load
+    // and count the row's confidences: the two chains overlap.
+    int q = -1, Kq = 0, bq = 0;
+    float th = 0.0f;
+    bool ok = false;
+    if (tid == 0) {
+        s_n = 0;
+        s_masked = 0;
+        q = row_req[row];
+        ok = q >= 0 && q < R.n_req;
+        if (ok) {
+            Kq = R.K[q];
+            bq = R.b[q];
+            th = R.threshold[q];
+        }
     }
-    nm = wave_sum_i(nm);
-    ns = wave_sum_i(ns);
+    int nm = 0, ns = 0;
+    if (tid >= 64) {
+        for (int j = tid - 64; j < L; j += kThreads - 64) {
+            const float c = conf[(int64_t)row * L + j];
+            s_c[j] = c;
+            ns += c >= 0.0f;
+            nm += mask_after[(int64_t)row * L + j] != 0;
+        }
+        nm = wave_sum_i(nm);
+        ns = wave_sum_i(ns);
+    }
     __syncthreads();
-    if ((tid & 63) == 0) {
+    if (tid >= 64 && (tid & 63) == 0) {
         atomicAdd(&s_masked, nm);
         atomicAdd(&s_n, ns);
     }
@@ -57,6 +76,7 @@ __global__ __launch_bounds__(kThreads) void features_kernel(int32_t L, const int
         const float c = s_c[j];
         if (c >= 0.0f) {
             int rank = 0;
+#pragma unroll 8
             for (int i = 0; i < L; ++i) {
                 const float ci = s_c[i];
                 rank += ci >= 0.0f && (ci < c || (ci == c && i < j));
@@ -67,17 +87,16 @@ __global__ __launch_bounds__(kThreads) void features_kernel(int32_t L, const int
     __syncthreads();
     if (tid != 0) return;
     float *f = out + (int64_t)row * kFeatures;
-    const int q = row_req[row];
-    if (q < 0 || q >= R.n_req || R.K[q] < 1) {
+    if (!ok || Kq < 1) {
         set_status(status, DLLM_ERR_ARG);
         for (int k = 0; k < kFeatures; ++k) store_nan(f + k);
         return;
     }
-    const int K = R.K[q], b = R.b[q], n = s_n;
+    const int n = s_n;
     const int unmasked = L - s_masked;
-    f[0] = R.threshold[q];
-    f[1] = (float)((int64_t)K * L);
-    f[2] = (float)(((double)b * L + unmasked) / ((double)K * L));
+    f[0] = th;
+    f[1] = (float)((int64_t)Kq * L);
+    f[2] = (float)(((double)bq * L + unmasked) / ((double)Kq * L));
     f[3] = (float)((double)unmasked / L);
     if (n == 0) {
         for (int k = 4; k < kFeatures; ++k) store_nan(f + k);
