@@ -13,11 +13,12 @@
 // workgroup the waves take chunks one at a time from an LDS counter: the sequencer favours older
 // waves when they compete for the memory pipe, so a fixed split per wave leaves the young ones
 // finishing last, while a shared counter lets every wave of the unit finish within about one chunk
-// of the others.  (Global atomics would do the same across units but cost a memory round trip each
-// and serialise on one address.)  One wavefront reduces one chunk: 64 lanes issue kVPL coalesced
-// 16-byte non-temporal loads each (1 KiB per wave instruction), the next chunk's loads go out
-// before this chunk's arithmetic, each element costs one FMA and one v_exp (sum of
-// exp2(x*log2e - max*log2e)), and lanes combine through DPP.  The chunk partial stays in a lane
+// of the others.  (Global atomics could balance across units too, but while the logits stream one
+// takes microseconds to return, longer than a wave spends on a chunk.)  One wavefront reduces one
+// chunk: 64 lanes issue kVPL coalesced 16-byte non-temporal loads each (1 KiB per wave
+// instruction), the next chunk's loads go out before this chunk's arithmetic, each element costs
+// an unpack, a share of a max3, one FMA, one v_exp and one add (sum of exp2(x*log2e - max*log2e)),
+// and lanes combine through DPP.  The chunk partial stays in a lane
 // register until the wave has 64 of them or runs out of chunks, then they leave in one store: a
 // store between the loads of consecutive chunks would hold back every later load until it
 // completed.  No MFMA: there is no contraction here.
