@@ -25,6 +25,7 @@ import hashlib
 import json
 import multiprocessing as mp
 import os
+import re
 import sys
 import time
 
@@ -34,18 +35,27 @@ sys.path.insert(0, ROOT)
 METRIC = "masked positions scored/sec + logits HBM GB/s (fraction of MI355X peak), 1 GPU"
 PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_dream_dynamic_traffic.json")
-# the scoring kernel's sources: the traffic figure is reported only while these are unchanged
-SCORE_SRC = [os.path.join(ROOT, "confidence_block_unmasking_amd", "csrc", f) for f in ("score.hip", "step_common.h")]
+# the scoring kernel's sources (with what they include): the traffic figure is reported only while
+# their code, comments and spacing aside, is unchanged
+SCORE_SRC = [os.path.join(ROOT, "confidence_block_unmasking_amd", "csrc", f) for f in ("score.hip", "step_common.h",
+                                                                                      "common.h")] + \
+            [os.path.join(ROOT, "include", "dllm.h")]
 SCORE_KERNEL = "score_kernel"
 COPY_MIB = 256
 EV_EVERY = 8          # steps between two HIP-event samples of the scoring kernel
 
 
 def _sha(paths):
+    """SHA-256 of the sources' code: comments removed and spacing collapsed, so that editing a comment
+    does not void a measurement taken on the same code."""
     h = hashlib.sha256()
     for path in paths:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
+        h.update(b"\0")
     return h.hexdigest()
 
 
