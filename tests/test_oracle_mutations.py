@@ -53,6 +53,19 @@ MUTATIONS = [
     ("oracle/shard.py", "a = min(t[1] for t in triples if t[0] == m)", "a = max(t[1] for t in triples if t[0] == m)",
      SHARD),
     ("oracle/shard.py", "S = sum(t[2] * np.exp(t[0] - m) for t in triples)", "S = sum(t[2] for t in triples)", SHARD),
+    # a dropped term, a shifted or transposed index, a flipped test: one more of each kind per module
+    ("oracle/step.py", "S = float(np.sum(np.exp(x - m)))", "S = float(np.sum(np.exp(x[1:] - m)))", STEP),
+    ("oracle/pack.py", "box_valid[r, pad:] = 1", "box_valid[r, pad + 1:] = 1", PACK),
+    ("oracle/pack.py", "tau[r] = threshold[q]", "tau[r] = threshold[r]", PACK),
+    ("oracle/compact.py", "arena[block_slice(q, b[q])] = box_ids[r, W - L:W]",
+     "arena[block_slice(q, b[q])] = box_ids[r, W - L - 1:W - 1]", PACK),
+    ("oracle/compact.py", "hit_eos = eos_id >= 0 and bool(np.any(committed == eos_id))",
+     "hit_eos = eos_id >= 0 and bool(np.all(committed == eos_id))", PACK),
+    ("oracle/loop.py", 'trace["idle_request_steps"] += int(np.sum(~(msk != 0).any(axis=1)))',
+     'trace["idle_request_steps"] += int(np.sum((msk != 0).any(axis=1)))', LOOP),
+    ("oracle/features.py", "f[3] = unmasked / L", "f[3] = (L - unmasked) / L", FEAT),
+    ("oracle/shard.py", "o += base + (1 if t < rem else 0)", "o += base + (1 if t <= rem else 0)", SHARD),
+    ("oracle/quota.py", "return min(m, ks[t])", "return ks[t]", QUOTA),
 ]
 
 

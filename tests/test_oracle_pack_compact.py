@@ -69,6 +69,8 @@ def test_pack_invariants_random():
             b = int(rng.integers(0, 3))
             reqs.append((p, b, list(rng.integers(0, 50, p + (b + 1) * L))))
         st = _table(reqs, L)
+        st["threshold"] = rng.choice(np.array([0.5, 0.6, 0.7, 0.8, 0.9], np.float32), n)
+        st["blk_mask"] = (rng.random((n, L)) < 0.5).astype(np.uint8)
         perm = rng.permutation(n)
         st["row_req"] = perm.astype(np.int64)
         W = opack.box_width(perm, n, st["p"], st["b"], L)
@@ -89,6 +91,9 @@ def test_pack_invariants_random():
             assert np.all(pos[valid == 0] == 0)
             assert out["box_ids"][r, valid == 1].tolist() == reqs[q][2]
             assert np.all(out["box_ids"][r, valid == 0] == -1)
+            # the per-row views follow the row's request, not the row index
+            assert out["threshold"][r] == st["threshold"][q] and out["p"][r] == st["p"][q]
+            assert out["b"][r] == st["b"][q] and np.array_equal(out["mask"][r], st["blk_mask"][q])
 
 
 def test_pack_rejects_too_narrow_box():
