@@ -66,6 +66,14 @@ MUTATIONS = [
     ("oracle/features.py", "f[3] = unmasked / L", "f[3] = (L - unmasked) / L", FEAT),
     ("oracle/shard.py", "o += base + (1 if t < rem else 0)", "o += base + (1 if t <= rem else 0)", SHARD),
     ("oracle/quota.py", "return min(m, ks[t])", "return ks[t]", QUOTA),
+    ("oracle/compact.py", "                arena[block_slice(q, b[q])] = mask_id\n                blk_mask[q] = 1",
+     "                blk_mask[q] = 1", PACK),
+    ("oracle/compact.py", "        state[q] = ACTIVE\n        b[q] = 0", "        state[q] = ACTIVE", PACK),
+    ("oracle/features.py", "        f[7] = c.mean()", "        f[7] = np.median(c)", FEAT),
+    ("oracle/loop.py", '            if mode == "fdfo" and out["done"].any():', '            if mode == "fdfo" and out["done"].all():',
+     LOOP),
+    ("oracle/shard.py", "    return m, offset + a, S", "    return m, a, S", SHARD),
+    ("oracle/quota.py", "    for j in js[:max(0, int(k))]:", "    for j in js[:max(0, int(k) - 1)]:", QUOTA),
 ]
 
 

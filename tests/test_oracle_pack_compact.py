@@ -261,6 +261,8 @@ def test_compact_in_place_reuse_and_hole_filling():
     done = np.array([0, 1, 0, 1, 0], np.uint8)
     mask = np.ones((5, L), np.uint8)
     mask[done == 1] = 0
+    o1 = int(st["arena_off"][1])
+    st["arena"][o1 + 1 + L:o1 + 1 + 2 * L] = 77                 # stale contents of the next block
     meta = ocompact.compact(st, 5, L, W, -5, -1, 0, 5, box_ids=box, mask=mask, done=done)
     # request 1 advanced to block 1 and keeps row 1; request 3 evicted; row 3 refilled from the tail
     assert meta["rows"] == 4 and meta["n_evicted"] == 1 and meta["W"] == 1 + 2 * L
@@ -269,6 +271,25 @@ def test_compact_in_place_reuse_and_hole_filling():
     assert st["blk_mask"][1].tolist() == [1, 1]
     blk1 = st["arena"][st["arena_off"][1] + 1 + L:st["arena_off"][1] + 1 + 2 * L]
     assert np.all(blk1 == -5)                                   # fresh, fully masked block
+
+
+def test_admission_opens_block_zero_whatever_the_table_held():
+    # an admitted request starts at block 0 with a fully masked block, whatever its b, block-0
+    # tokens and block mask held before ([BlockServe] §II-C: admission; §II-E: blocks start masked)
+    L = 2
+    st = _table([(2, 0, [])], L, K=[3], mask_id=-5)
+    st["row_req"] = np.full(2, -1, np.int64)
+    st["state"][0] = 0
+    st["queue"] = np.array([0], np.int64)
+    st["b"][0] = 2
+    o = int(st["arena_off"][0])
+    st["arena"][o + 2:o + 2 + L] = 77
+    st["blk_mask"][0] = 0
+    meta = ocompact.compact(st, 0, L, 0, -5, -1, 0, 2)
+    assert meta["rows"] == 1 and meta["n_admitted"] == 1 and st["row_req"][0] == 0
+    assert st["b"][0] == 0 and st["state"][0] == 1
+    assert np.all(st["arena"][o + 2:o + 2 + L] == -5) and st["blk_mask"][0].tolist() == [1, 1]
+    assert meta["W"] == 2 + L
 
 
 def test_compact_eos_evicts_early():
