@@ -192,6 +192,24 @@ def test_loop_at_the_row_limit():
     assert res["steps"] >= 2
 
 
+def test_loop_overwrites_stale_table_contents():
+    """Blocks that compact opens (the next block of an advancing request, block 0 of an admitted
+    one) are written in full: stale tokens beyond each request's current block, and a stale block
+    index and block mask of the queued requests, must not show through."""
+    w = configs.small(L=4, V=64, n_act=2, n_q=6, K=3, seed=23, dtype="fp32", rows_cap=3, p_range=(1, 7))
+    w.row_req = np.concatenate([w.row_req[:w.rows], np.full(3 - w.rows, -1, np.int32)])
+    for q in range(w.n_req):
+        start = int(w.arena_off[q]) + int(w.p[q]) + (int(w.b[q]) + 1) * w.L
+        end = int(w.arena_off[q]) + int(w.p[q]) + int(w.K[q]) * w.L
+        w.arena[start:end] = 777
+    for q in w.queue:
+        w.b[q] = int(w.K[q]) - 1
+        o = int(w.arena_off[q]) + int(w.p[q])
+        w.arena[o:o + w.L] = 777
+        w.blk_mask[q] = 0
+    lockstep_run(w, full_score_max=10**9, label="stale")
+
+
 def test_loop_end_of_sequence_evicts_early():
     """With an end-of-sequence id, requests whose committed block holds it leave before block K."""
     w = configs.small(L=4, V=16, n_act=0, n_q=10, K=4, seed=32, dtype="fp32", rows_cap=4, p_range=(1, 8))
