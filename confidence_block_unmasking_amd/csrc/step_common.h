@@ -14,6 +14,9 @@ namespace dllm {
 #ifndef DLLM_STEP_WAVES
 #define DLLM_STEP_WAVES 8
 #endif
+#ifndef DLLM_STEP_ACC
+#define DLLM_STEP_ACC 4               // running sums per lane in the chunk reduction (a power of two)
+#endif
 
 constexpr int kWaves = DLLM_STEP_WAVES;       // waves per scoring workgroup (one workgroup per CU)
 constexpr int kThreads = 64 * kWaves;
@@ -179,19 +182,25 @@ __device__ __forceinline__ Part reduce_lanes(float (&x)[kVPL][E], int vb) {
 #pragma unroll
     for (int k = 1; k < kVPL; ++k) m = fmaxf(m, vm[k]);
     const float nml = (m == -INFINITY) ? 0.0f : -m * kLog2e;
-    float s0 = 0.0f, s1 = 0.0f;
+    // DLLM_STEP_ACC independent running sums (the adds are the only serial chain of the loop)
+    float acc[DLLM_STEP_ACC];
+#pragma unroll
+    for (int a = 0; a < DLLM_STEP_ACC; ++a) acc[a] = 0.0f;
 #pragma unroll
     for (int k = 0; k < kVPL; ++k) {
 #pragma unroll
-        for (int e = 0; e < E; e += 2) {
-            s0 += __builtin_amdgcn_exp2f(fmaf(x[k][e], kLog2e, nml));
-            s1 += __builtin_amdgcn_exp2f(fmaf(x[k][e + 1], kLog2e, nml));
-        }
+        for (int e = 0; e < E; ++e)
+            acc[(k * E + e) % DLLM_STEP_ACC] += __builtin_amdgcn_exp2f(fmaf(x[k][e], kLog2e, nml));
+    }
+#pragma unroll
+    for (int w = DLLM_STEP_ACC / 2; w >= 1; w /= 2) {
+#pragma unroll
+        for (int a = 0; a < w; ++a) acc[a] += acc[a + w];
     }
     Part r;
     r.m = red_max_bc(m);
     const float scale = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m - r.m) * kLog2e);
-    r.s = red_sum_bc((s0 + s1) * scale);
+    r.s = red_sum_bc(acc[0] * scale);
     int elem = 0x7FFFFFFF;
     if (r.m != -INFINITY) {
         int kw = 0, lw = 0;
