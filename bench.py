@@ -101,13 +101,18 @@ def cpu_baseline(cpu_seconds):
     wall = time.perf_counter() - t0
     slots = sum(s for s, _ in res)
     busy = max(t for _, t in res)
+    # the same oracle on one core, over every row in turn
+    one_secs = max(1.0, cpu_seconds / 4)
+    slots1, busy1 = _cpu_worker((list(range(w.rows)), one_secs))
     _CPU.clear()
     value = slots / busy
     return {"value": value, "unit": "masked positions/s", "cores": len(res), "kind": "oracle",
             "sample": f"{slots} masked-slot scorings of the same 64-row step (rows round-robin over {len(res)} "
                       f"processes, one thread each, {per:.1f} s each, repeated passes; {wall:.1f} s wall); "
                       "numpy float64; logits generation excluded",
-            "logits_GBps_equiv": value * w.V * w.elem_bytes / 1e9}
+            "logits_GBps_equiv": value * w.V * w.elem_bytes / 1e9,
+            "one_core": {"value": slots1 / busy1, "sample": f"{slots1} masked-slot scorings in {busy1:.1f} s, one "
+                                                             "process"}}
 
 
 # ---- HBM byte counters -------------------------------------------------------------------------
@@ -319,6 +324,30 @@ def run_gpu(args):
     if len(metas) != 1:
         raise SystemExit("timed steps from the same start state produced different layouts")
     elapsed = t1 - t0
+    # dllm_step (score + decide) from a cold cache, outside the timed region: before each launch a
+    # 1 GiB buffer is written, which evicts the logits from L2 and the 256 MB Infinity Cache
+    cold_us = None
+    if args.cold > 0 and args.shards <= 1:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cold_ev = []
+        for k in range(args.cold + 2):
+            flush.fill_(k & 0xFF)
+            e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            e[0].record()
+            rc |= lib.dllm_step_score(*score_args[k % args.rotate])
+            rc |= decide_fn(*decide_args)
+            e[1].record()
+            if k >= 2:
+                cold_ev.append(e)
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise SystemExit(f"library error rc={rc}: {_lib.last_error()}")
+        cms = np.array([a.elapsed_time(b) for a, b in cold_ev]) * 1e3
+        cold_us = {"launches": int(cms.size), "p10": float(np.percentile(cms, 10)),
+                   "median": float(np.median(cms)), "p90": float(np.percentile(cms, 90)),
+                   "what": "dllm_step_score + dllm_step_decide between two HIP events, each launch after a "
+                           "1 GiB write that evicts L2 and the Infinity Cache"}
+        del flush
     kern_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(args.warmup, n_total) if k in ev])
     kern_s = float(kern_ms.mean()) / 1e3
     step_bytes = M * V * 2
@@ -349,6 +378,7 @@ def run_gpu(args):
         "score_kernel_us": {"samples": int(kern_ms.size), "mean": float(kern_ms.mean()) * 1e3, "p10": float(np.percentile(kern_ms, 10)) * 1e3,
                             "p50": float(np.percentile(kern_ms, 50)) * 1e3,
                             "p90": float(np.percentile(kern_ms, 90)) * 1e3},
+        **({"dllm_step_cold_us": cold_us} if cold_us else {}),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": stored_traffic(M) if args.shards <= 1 and args.rule == "threshold" else None},
@@ -376,14 +406,20 @@ def run_loop(name, mode):
     sess = Session.from_workload(w)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    st = sess.run(mode, fwd)
+    st = sess.run(mode, fwd, timed=True)
     torch.cuda.synchronize()
     sec = time.perf_counter() - t0
+    ph = sess.phase_ms()
+    ph["host"] = sec * 1e3 - sum(ph.values())
     keys = ("steps", "request_steps", "idle_request_steps", "rounds", "positions_scored", "evicted", "admitted",
             "max_cost")
     return {"loop": w.name, "mode": mode, "seconds": sec,
             "masked_positions_per_s": st["positions_scored"] / sec, **{k: st[k] for k in keys},
-            "note": "wall time includes the synthetic forward (logits generation) of every step"}
+            "phase_ms": ph,
+            "step_logits_GBps": st["positions_scored"] * w.V * w.elem_bytes / (ph["step"] / 1e3) / 1e9,
+            "note": "wall time includes the synthetic forward (logits generation) of every step; phase_ms sums "
+                    "HIP events around every forward, dllm_step, dllm_pack and dllm_compact, and host is the "
+                    "rest of the wall time (read-backs of done and mask, scheduling, launches)"}
 
 
 def main():
@@ -397,6 +433,8 @@ def main():
                     help="unmasking rule: LowConfidence threshold (default) or the fixed per-step quota")
     ap.add_argument("--steps-per-block", type=int, default=32, help="diffusion steps per block (quota rule)")
     ap.add_argument("--shards", type=int, default=1, help="score the vocabulary in this many slices and combine")
+    ap.add_argument("--cold", type=int, default=100,
+                    help="after the timed loop, time this many single dllm_step launches from a flushed cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--features", action="store_true",
                     help="also compute the step-predictor features of every row after each step")

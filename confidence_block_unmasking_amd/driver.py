@@ -63,7 +63,8 @@ class Session:
         self.W = 0
         self.stats = dict(steps=0, request_steps=0, positions_scored=0, compacts=0, packs=0, rounds=0,
                           idle_request_steps=0, max_cost=0, evicted=0, admitted=0)
-        self.step_events = []          # (start, end) cuda events of each dllm_step, when timing
+        # (start, end) events around each library call and each forward, when a run is timed
+        self.events = {"forward": [], "step": [], "pack": [], "compact": []}
 
     @classmethod
     def from_workload(cls, w, device="cuda", logits=None, eos_id=-1):
@@ -84,13 +85,31 @@ class Session:
         if s != 0:
             raise api.DllmError(s, where, "(device status)")
 
+    def _timed(self, phase, timed, fn):
+        """fn(), bracketed by two events on the current stream when timed (the events cover the
+        device work fn enqueues, not host work after it)."""
+        if not timed:
+            return fn()
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        ev[0].record()
+        out = fn()
+        ev[1].record()
+        self.events[phase].append(ev)
+        return out
+
+    def phase_ms(self):
+        """Total milliseconds of each timed phase so far (synchronises)."""
+        torch.cuda.synchronize()
+        return {k: float(sum(a.elapsed_time(b) for a, b in v)) for k, v in self.events.items()}
+
     # ---- the three library calls ----------------------------------------------------------------
-    def compact(self, with_box=True):
+    def compact(self, with_box=True, timed=False):
         kw = {}
         if with_box and self.rows > 0:
             kw = dict(box_ids=self.box_ids, mask=self.masks[self.cur], done=self.done)
-        api.dllm_compact(self.rows, self.L, self.W, self.mask_id, self.eos_id, self.row_req, self.rows_cap, self.reqs,
-                         self.queue, self.budget, self.meta, self.status, **kw)
+        self._timed("compact", timed, lambda: api.dllm_compact(
+            self.rows, self.L, self.W, self.mask_id, self.eos_id, self.row_req, self.rows_cap, self.reqs,
+            self.queue, self.budget, self.meta, self.status, **kw))
         m = api.read_meta(self.meta)
         self.check_status("dllm_compact")
         self.rows, self.W = m["rows"], m["W"]
@@ -100,25 +119,18 @@ class Session:
         self.stats["max_cost"] = max(self.stats["max_cost"], m["cost"])
         return m
 
-    def pack(self):
-        api.dllm_pack(self.rows, self.L, self.W, self.pad_id, self.row_req, self.reqs, self.box_ids,
-                      self.masks[self.cur], self.tau, self.p_rows, self.b_rows, self.status, box_valid=self.box_valid,
-                      box_pos=self.box_pos)
+    def pack(self, timed=False):
+        self._timed("pack", timed, lambda: api.dllm_pack(
+            self.rows, self.L, self.W, self.pad_id, self.row_req, self.reqs, self.box_ids, self.masks[self.cur],
+            self.tau, self.p_rows, self.b_rows, self.status, box_valid=self.box_valid, box_pos=self.box_pos))
         self.stats["packs"] += 1
 
     def step(self, timed=False):
         nxt = 1 - self.cur
-        ev = None
-        if timed:
-            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            ev[0].record()
-        api.dllm_step(self.logits, self.box(), self.masks[self.cur], self.masks[nxt], self.tau, self.done,
-                      self.accept, self.workspace, self.status, p=self.p_rows, b=self.b_rows, conf=self.conf,
-                      argmax=self.argmax, rows=self.rows, L=self.L, V=self.V, pos_stride=self.V,
-                      row_stride=self.L * self.V)
-        if timed:
-            ev[1].record()
-            self.step_events.append(ev)
+        self._timed("step", timed, lambda: api.dllm_step(
+            self.logits, self.box(), self.masks[self.cur], self.masks[nxt], self.tau, self.done, self.accept,
+            self.workspace, self.status, p=self.p_rows, b=self.b_rows, conf=self.conf, argmax=self.argmax,
+            rows=self.rows, L=self.L, V=self.V, pos_stride=self.V, row_stride=self.L * self.V))
         self.cur = nxt
 
     def features(self):
@@ -136,11 +148,12 @@ class Session:
         "handback" (first-done-first-out that hands control back to the scheduler after every step,
         the behaviour the in-place re-loop removes).  forward(session) fills session.logits for the
         current box.  on_step(session, info) is called after every step with the host copies (done,
-        new mask) — the test harness uses it to check each step.  Returns self.stats."""
+        new mask) — the test harness uses it to check each step.  timed: bracket every forward,
+        step, pack and compact with events (totals from phase_ms()).  Returns self.stats."""
         assert mode in ("sync", "fdfo", "handback")
-        self.compact(with_box=False)                 # admission at the start of the run
+        self.compact(with_box=False, timed=timed)    # admission at the start of the run
         while self.rows > 0:
-            self.pack()
+            self.pack(timed=timed)
             mask_host = self.mask().cpu().numpy()
             while True:
                 if self.stats["steps"] >= max_steps:
@@ -149,7 +162,7 @@ class Session:
                 self.stats["request_steps"] += self.rows
                 self.stats["idle_request_steps"] += int((~masked_rows).sum())
                 self.stats["positions_scored"] += int((mask_host != 0).sum())
-                forward(self)
+                self._timed("forward", timed, lambda: forward(self))
                 self.step(timed=timed)
                 done = self.done[:self.rows].cpu().numpy()
                 mask_host = self.mask().cpu().numpy()
@@ -164,7 +177,7 @@ class Session:
                 if mode == "handback":
                     break
             self.stats["rounds"] += 1
-            self.compact(with_box=True)
+            self.compact(with_box=True, timed=timed)
         return self.stats
 
     # ---- host views for tests -----------------------------------------------------------------

@@ -325,3 +325,27 @@ def test_loop_modes_same_tokens_and_oracle_traces():
         print(f"{mode}: {dict((k, stats[k]) for k in ('steps', 'request_steps', 'idle_request_steps', 'rounds'))}",
               flush=True)
     assert np.array_equal(arenas["sync"], arenas["fdfo"]) and np.array_equal(arenas["fdfo"], arenas["handback"])
+
+
+def test_loop_phase_timing_brackets_every_call():
+    """A timed run brackets every forward, step, pack and compact with events; the accounting and
+    the final tables are those of the untimed run."""
+    T = [3, 5, 2]
+    runs = {}
+    for timed in (False, True):
+        sess = _abc_session(T)
+        stats = dict(sess.run("fdfo", lambda s: s.logits.zero_(), timed=timed))
+        runs[timed] = (stats, sess.host_table())
+        if timed:
+            ev = sess.events
+            assert len(ev["step"]) == len(ev["forward"]) == stats["steps"]
+            assert len(ev["pack"]) == stats["packs"]
+            assert len(ev["compact"]) == stats["compacts"]
+            ph = sess.phase_ms()
+            assert set(ph) == {"forward", "step", "pack", "compact"}
+            assert all(v > 0 for v in ph.values()), ph
+        else:
+            assert all(len(v) == 0 for v in sess.events.values())
+    assert runs[False][0] == runs[True][0]
+    for k in ("row_req", "b", "state", "arena", "blk_mask"):
+        assert np.array_equal(runs[False][1][k], runs[True][1][k]), k
