@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(StepParams P, int win) 
 }
 
 
-dllm_status launch_score(const StepParams &P, dllm_dtype dtype, hipStream_t st) {
+dllm_status launch_score(const StepParams &P, int32_t dtype, hipStream_t st) {
     const int es = dtype == DLLM_BF16 ? 2 : 4;
     const int64_t S = (int64_t)P.rows * P.L;
     const int NC = P.NC;

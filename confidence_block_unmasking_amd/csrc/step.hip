@@ -42,7 +42,7 @@ namespace {
 using namespace dllm;
 
 // Checks shared by the three entry points; fills P's shape fields.  `who` names the caller.
-dllm_status check_shape(const char *who, dllm_dtype dtype, int32_t rows, int32_t L, int32_t V, void *workspace,
+dllm_status check_shape(const char *who, int32_t dtype, int32_t rows, int32_t L, int32_t V, void *workspace,
                         StepParams &P) {
     if (dtype != DLLM_FP32 && dtype != DLLM_BF16) return fail(DLLM_ERR_DTYPE, "%s: unknown dtype %d", who, (int)dtype);
     if (rows < 0) return fail(DLLM_ERR_ARG, "%s: rows < 0", who);
@@ -60,7 +60,7 @@ dllm_status check_shape(const char *who, dllm_dtype dtype, int32_t rows, int32_t
 }
 
 // The workspace check, after every other argument check.
-dllm_status check_workspace(const char *who, dllm_dtype dtype, const void *workspace, size_t workspace_bytes,
+dllm_status check_workspace(const char *who, int32_t dtype, const void *workspace, size_t workspace_bytes,
                             const StepParams &P) {
     if (P.rows == 0) return DLLM_OK;
     int NV, NC;
@@ -73,7 +73,7 @@ dllm_status check_workspace(const char *who, dllm_dtype dtype, const void *works
     return DLLM_OK;
 }
 
-dllm_status check_score(const char *who, const void *logits, dllm_dtype dtype, int64_t pos_stride, int64_t row_stride,
+dllm_status check_score(const char *who, const void *logits, int32_t dtype, int64_t pos_stride, int64_t row_stride,
                         const uint8_t *mask_in, int32_t *status, StepParams &P) {
     if (pos_stride < P.V || row_stride < (int64_t)P.L * pos_stride)
         return fail(DLLM_ERR_ARG, "%s: strides too small (pos %lld, row %lld)", who, (long long)pos_stride,
@@ -119,14 +119,14 @@ dllm_status check_decide(const char *who, int32_t *input_ids, int32_t W, const u
 }  // namespace
 
 
-extern "C" size_t dllm_step_workspace_bytes(int32_t rows, int32_t L, int32_t V, dllm_dtype dtype) {
+extern "C" size_t dllm_step_workspace_bytes(int32_t rows, int32_t L, int32_t V, int32_t dtype) {
     int NV, NC;
     size_t bytes;
     if (!shape_of(rows, L, V, dtype, NV, NC, bytes)) return 0;
     return bytes;
 }
 
-extern "C" dllm_status dllm_step(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+extern "C" dllm_status dllm_step(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
                                  int64_t row_stride, int32_t rows, int32_t L, int32_t V, int32_t *input_ids,
                                  int32_t W, const uint8_t *mask_in, uint8_t *mask_out, const float *threshold,
                                  const int32_t *p, const int32_t *b, float *conf, int32_t *argmax,
@@ -145,7 +145,7 @@ extern "C" dllm_status dllm_step(void *stream, const void *logits, dllm_dtype dt
     return launch_decide(P, (hipStream_t)stream, P.S > 0 ? kRuleQuota : kRuleThreshold);
 }
 
-extern "C" dllm_status dllm_step_score(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+extern "C" dllm_status dllm_step_score(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
                                        int64_t row_stride, int32_t rows, int32_t L, int32_t V,
                                        const uint8_t *mask_in, void *workspace, size_t workspace_bytes,
                                        int32_t *status) {
@@ -157,7 +157,7 @@ extern "C" dllm_status dllm_step_score(void *stream, const void *logits, dllm_dt
     return launch_score(P, dtype, (hipStream_t)stream);
 }
 
-extern "C" dllm_status dllm_step_decide(void *stream, dllm_dtype dtype, int32_t rows, int32_t L, int32_t V,
+extern "C" dllm_status dllm_step_decide(void *stream, int32_t dtype, int32_t rows, int32_t L, int32_t V,
                                         int32_t *input_ids, int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
                                         const float *threshold, const int32_t *p, const int32_t *b, float *conf,
                                         int32_t *argmax, uint8_t *done, int32_t *accept_len, void *workspace,
@@ -172,7 +172,7 @@ extern "C" dllm_status dllm_step_decide(void *stream, dllm_dtype dtype, int32_t 
     return launch_decide(P, (hipStream_t)stream, P.S > 0 ? kRuleQuota : kRuleThreshold);
 }
 
-extern "C" dllm_status dllm_step_quota(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+extern "C" dllm_status dllm_step_quota(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
                                        int64_t row_stride, int32_t rows, int32_t L, int32_t V, int32_t *input_ids,
                                        int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
                                        int32_t steps_per_block, const int32_t *p, const int32_t *b, float *conf,
@@ -192,7 +192,7 @@ extern "C" dllm_status dllm_step_quota(void *stream, const void *logits, dllm_dt
     return launch_decide(P, (hipStream_t)stream, P.S > 0 ? kRuleQuota : kRuleThreshold);
 }
 
-extern "C" dllm_status dllm_step_decide_quota(void *stream, dllm_dtype dtype, int32_t rows, int32_t L, int32_t V,
+extern "C" dllm_status dllm_step_decide_quota(void *stream, int32_t dtype, int32_t rows, int32_t L, int32_t V,
                                               int32_t *input_ids, int32_t W, const uint8_t *mask_in,
                                               uint8_t *mask_out, int32_t steps_per_block, const int32_t *p,
                                               const int32_t *b, float *conf, int32_t *argmax, uint8_t *done,
@@ -214,7 +214,7 @@ extern "C" size_t dllm_shard_triples_bytes(int32_t rows, int32_t L, int32_t n_sh
     return (size_t)rows * (size_t)L * (size_t)n_shards * sizeof(float4);
 }
 
-extern "C" dllm_status dllm_step_score_shard(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+extern "C" dllm_status dllm_step_score_shard(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
                                              int64_t row_stride, int32_t rows, int32_t L, int32_t V_shard,
                                              int32_t vocab_offset, int32_t shard, int32_t n_shards,
                                              const uint8_t *mask_in, void *workspace, size_t workspace_bytes,

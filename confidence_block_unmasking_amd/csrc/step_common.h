@@ -308,7 +308,7 @@ __device__ __forceinline__ int block_sum(int v, int *tmp) {
 }
 
 
-inline bool shape_of(int32_t rows, int32_t L, int32_t V, dllm_dtype dt, int &NV, int &NC, size_t &bytes) {
+inline bool shape_of(int32_t rows, int32_t L, int32_t V, int32_t dt, int &NV, int &NC, size_t &bytes) {
     if (rows < 0 || L < 1 || V < 1 || (dt != DLLM_FP32 && dt != DLLM_BF16)) return false;
     const int E = dt == DLLM_BF16 ? 8 : 4;
     const int64_t nv = ((int64_t)V + E - 1) / E;
@@ -320,7 +320,7 @@ inline bool shape_of(int32_t rows, int32_t L, int32_t V, dllm_dtype dt, int &NV,
 
 
 // Launchers (score.hip, decide.hip): enqueue the kernels for checked parameters.
-dllm_status launch_score(const StepParams &P, dllm_dtype dtype, hipStream_t st);
+dllm_status launch_score(const StepParams &P, int32_t dtype, hipStream_t st);
 // mode: kRuleThreshold / kRuleQuota apply the row's rule; kEmitTriples writes each masked slot's
 // merged (max, sum, global index) into P.triples at shard P.shard instead.
 constexpr int kRuleThreshold = 0, kRuleQuota = 1, kEmitTriples = 2;

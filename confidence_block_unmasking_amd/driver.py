@@ -62,7 +62,8 @@ class Session:
         self.logits = logits if logits is not None else torch.empty((n, self.L, self.V), dtype=dtype, device=device)
         self.W = 0
         self.stats = dict(steps=0, request_steps=0, positions_scored=0, compacts=0, packs=0, rounds=0,
-                          idle_request_steps=0, max_cost=0, evicted=0, admitted=0)
+                          idle_request_steps=0, max_cost=0, evicted=0, admitted=0, unmasked=0,
+                          fallback_row_steps=0, block_steps={})
         # (start, end) events around each library call and each forward, when a run is timed
         self.events = {"forward": [], "step": [], "pack": [], "compact": []}
 
@@ -140,7 +141,7 @@ class Session:
         return self.features_buf[:self.rows * api.N_FEATURES].view(self.rows, api.N_FEATURES)
 
     # ---- the loop rule ----------------------------------------------------------------------------
-    def run(self, mode, forward, max_steps=10**7, on_step=None, timed=False):
+    def run(self, mode, forward, max_steps=10**7, on_step=None, timed=False, max_rounds=0, metrics=False):
         """Drive compact -> pack -> (forward, step)* -> compact ... until queue and rows are empty.
 
         mode: "sync" (the batch runs until every block is done), "fdfo" (first-done-first-out with
@@ -149,27 +150,50 @@ class Session:
         the behaviour the in-place re-loop removes).  forward(session) fills session.logits for the
         current box.  on_step(session, info) is called after every step with the host copies (done,
         new mask) — the test harness uses it to check each step.  timed: bracket every forward,
-        step, pack and compact with events (totals from phase_ms()).  Returns self.stats."""
+        step, pack and compact with events (totals from phase_ms()).  max_rounds > 0 returns after
+        that many scheduler rounds, right after a compact, where snapshot() holds the whole state.
+        The stats always count the tokens unmasked; metrics=True also reads back the confidences and
+        the row map to count the row-steps decided by the fallback (no masked confidence above the
+        threshold) and the steps each finished block took (stats["block_steps"]: steps -> blocks).
+        Returns self.stats."""
         assert mode in ("sync", "fdfo", "handback")
         self.compact(with_box=False, timed=timed)    # admission at the start of the run
+        in_block = {}                                # request -> steps of its current block
         while self.rows > 0:
             self.pack(timed=timed)
             mask_host = self.mask().cpu().numpy()
+            if metrics:
+                tau_host = self.tau[:self.rows].cpu().numpy()
+                req_host = self.row_req[:self.rows].cpu().numpy()
             while True:
                 if self.stats["steps"] >= max_steps:
                     raise RuntimeError("step limit reached")
-                masked_rows = (mask_host != 0).any(axis=1)
+                masked = mask_host != 0
+                masked_rows = masked.any(axis=1)
                 self.stats["request_steps"] += self.rows
                 self.stats["idle_request_steps"] += int((~masked_rows).sum())
-                self.stats["positions_scored"] += int((mask_host != 0).sum())
+                self.stats["positions_scored"] += int(masked.sum())
                 self._timed("forward", timed, lambda: forward(self))
                 self.step(timed=timed)
                 done = self.done[:self.rows].cpu().numpy()
                 mask_host = self.mask().cpu().numpy()
                 self.check_status("dllm_step")
                 self.stats["steps"] += 1
+                unmasked = int(masked.sum()) - int((mask_host != 0).sum())
+                self.stats["unmasked"] += unmasked
+                if metrics:
+                    conf = self.conf[:self.rows * self.L].view(self.rows, self.L).cpu().numpy()
+                    above = (masked & (conf > tau_host[:, None])).any(axis=1)
+                    self.stats["fallback_row_steps"] += int((masked_rows & ~above).sum())
+                    for r in np.flatnonzero(masked_rows):
+                        q = int(req_host[r])
+                        in_block[q] = in_block.get(q, 0) + 1
+                        if done[r]:
+                            hist = self.stats["block_steps"]
+                            hist[in_block[q]] = hist.get(in_block[q], 0) + 1
+                            in_block[q] = 0
                 if on_step is not None:
-                    on_step(self, dict(done=done, mask=mask_host))
+                    on_step(self, dict(done=done, mask=mask_host, unmasked=unmasked))
                 if mode == "fdfo" and done.any():
                     break
                 if mode == "sync" and done.all():
@@ -178,7 +202,28 @@ class Session:
                     break
             self.stats["rounds"] += 1
             self.compact(with_box=True, timed=timed)
+            if max_rounds and self.stats["rounds"] >= max_rounds:
+                break
         return self.stats
+
+    # ---- checkpoint / resume ----------------------------------------------------------------------
+    def snapshot(self):
+        """Host copy of everything a later run needs, taken between two scheduler rounds (after a
+        compact): the request table, token arena, block masks, row map, queue and active rows, plus
+        the fixed parameters.  The box, per-row views and step buffers are rebuilt by the next pack."""
+        h = self.host_table()
+        return dict(h, rows=self.rows, L=self.L, V=self.V, dtype=self.dtype, rows_cap=self.rows_cap,
+                    budget=self.budget, mask_id=self.mask_id, pad_id=self.pad_id, eos_id=self.eos_id)
+
+    @classmethod
+    def from_snapshot(cls, snap, device="cuda", logits=None):
+        """A session that continues from snapshot(): run() then carries on where the other stopped
+        (its opening admission admits nothing the last compact did not)."""
+        return cls(snap["p"], snap["K"], snap["b"], snap["state"], snap["threshold"], snap["arena_off"],
+                   snap["arena"], snap["blk_mask"], snap["row_req"], snap["rows"], snap["queue"], L=snap["L"],
+                   V=snap["V"], dtype=snap["dtype"], rows_cap=snap["rows_cap"], budget=snap["budget"],
+                   mask_id=snap["mask_id"], pad_id=snap["pad_id"], eos_id=snap["eos_id"], device=device,
+                   logits=logits)
 
     # ---- host views for tests -----------------------------------------------------------------
     def host_table(self):

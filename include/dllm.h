@@ -38,6 +38,9 @@ typedef enum {
     DLLM_ERR_HIP = 5        /* a HIP call failed (text from dllm_last_error) */
 } dllm_status;
 
+/* Logits element types.  Entry points take the value as an int32_t `dtype` (the size of a C enum is
+ * the compiler's choice, and any other value must be rejected, not assumed away): anything but these
+ * two returns DLLM_ERR_DTYPE, or 0 from dllm_step_workspace_bytes. */
 typedef enum { DLLM_FP32 = 0, DLLM_BF16 = 1 } dllm_dtype;
 
 /* Limits (checked synchronously). */
@@ -126,7 +129,7 @@ typedef struct {
  * rows > DLLM_MAX_ROWS, rows*L > DLLM_MAX_POSITIONS), DLLM_ERR_DTYPE, DLLM_ERR_HIP.
  * rows == 0 is a no-op returning DLLM_OK.  Work: two kernels on `stream` (scoring, then the
  * per-row decision); the call returns after enqueueing both. */
-dllm_status dllm_step(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+dllm_status dllm_step(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
                       int64_t row_stride, int32_t rows, int32_t L, int32_t V, int32_t *input_ids,
                       int32_t W, const uint8_t *mask_in, uint8_t *mask_out, const float *threshold,
                       const int32_t *p, const int32_t *b, float *conf, int32_t *argmax, uint8_t *done,
@@ -134,7 +137,7 @@ dllm_status dllm_step(void *stream, const void *logits, dllm_dtype dtype, int64_
 
 /* Bytes of workspace dllm_step (or the pair below) needs for this shape (0 for invalid
  * arguments). */
-size_t dllm_step_workspace_bytes(int32_t rows, int32_t L, int32_t V, dllm_dtype dtype);
+size_t dllm_step_workspace_bytes(int32_t rows, int32_t L, int32_t V, int32_t dtype);
 
 /* dllm_step_score and dllm_step_decide — dllm_step in its two halves, for callers that time,
  * overlap or schedule them apart.  Calling dllm_step_score, then dllm_step_decide on the same
@@ -148,10 +151,10 @@ size_t dllm_step_workspace_bytes(int32_t rows, int32_t L, int32_t V, dllm_dtype 
  * dllm_step_decide: merges those partials in a fixed order into conf and argmax and applies the
  * LowConfidence rule, with the outputs and conditions of dllm_step.  It reads no logits.
  * Errors: those of dllm_step that concern each half's own arguments. */
-dllm_status dllm_step_score(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+dllm_status dllm_step_score(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
                             int64_t row_stride, int32_t rows, int32_t L, int32_t V, const uint8_t *mask_in,
                             void *workspace, size_t workspace_bytes, int32_t *status);
-dllm_status dllm_step_decide(void *stream, dllm_dtype dtype, int32_t rows, int32_t L, int32_t V,
+dllm_status dllm_step_decide(void *stream, int32_t dtype, int32_t rows, int32_t L, int32_t V,
                              int32_t *input_ids, int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
                              const float *threshold, const int32_t *p, const int32_t *b, float *conf,
                              int32_t *argmax, uint8_t *done, int32_t *accept_len, void *workspace,
@@ -167,12 +170,12 @@ dllm_status dllm_step_decide(void *stream, dllm_dtype dtype, int32_t rows, int32
  *   U = the k masked slots with the largest confidence, the lowest j on ties.
  * Write-back, done and accept_len as for dllm_step.  steps_per_block >= 1 (DLLM_ERR_ARG
  * otherwise); no threshold.  Other arguments and errors as for dllm_step / dllm_step_decide. */
-dllm_status dllm_step_quota(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+dllm_status dllm_step_quota(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
                             int64_t row_stride, int32_t rows, int32_t L, int32_t V, int32_t *input_ids,
                             int32_t W, const uint8_t *mask_in, uint8_t *mask_out, int32_t steps_per_block,
                             const int32_t *p, const int32_t *b, float *conf, int32_t *argmax, uint8_t *done,
                             int32_t *accept_len, void *workspace, size_t workspace_bytes, int32_t *status);
-dllm_status dllm_step_decide_quota(void *stream, dllm_dtype dtype, int32_t rows, int32_t L, int32_t V,
+dllm_status dllm_step_decide_quota(void *stream, int32_t dtype, int32_t rows, int32_t L, int32_t V,
                                    int32_t *input_ids, int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
                                    int32_t steps_per_block, const int32_t *p, const int32_t *b, float *conf,
                                    int32_t *argmax, uint8_t *done, int32_t *accept_len, void *workspace,
@@ -197,7 +200,7 @@ dllm_status dllm_step_decide_quota(void *stream, dllm_dtype dtype, int32_t rows,
  * Errors: as dllm_step_score / dllm_step_decide, plus DLLM_ERR_ARG for a shard outside
  * [0, n_shards), n_shards outside [1, DLLM_MAX_SHARDS], a negative vocab_offset or null triples. */
 size_t dllm_shard_triples_bytes(int32_t rows, int32_t L, int32_t n_shards);
-dllm_status dllm_step_score_shard(void *stream, const void *logits, dllm_dtype dtype, int64_t pos_stride,
+dllm_status dllm_step_score_shard(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
                                   int64_t row_stride, int32_t rows, int32_t L, int32_t V_shard,
                                   int32_t vocab_offset, int32_t shard, int32_t n_shards,
                                   const uint8_t *mask_in, void *workspace, size_t workspace_bytes,

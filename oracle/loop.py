@@ -27,14 +27,17 @@ from .step import step
 
 
 def run(st: dict, rows: int, L: int, mask_id: int, pad_id: int, dtype: str, budget: int, rows_cap: int,
-        mode: str, logits_fn, eos_id: int = -1, max_steps: int = 1_000_000):
+        mode: str, logits_fn, eos_id: int = -1, max_steps: int = 1_000_000, max_rounds: int = 0):
     """Drive pack -> (step)* -> compact until the queue and the active set are empty.
 
     st: request table (see compact()); rows: number of active rows on entry.
     logits_fn(row_req, b_rows, mask_rows) -> logits [rows, L, V] for the current box.
     Returns a trace dict: steps (batch steps), request_steps (rows stepped, summed over steps),
     idle_request_steps (rows stepped with no masked slot left), rounds (hand-backs to the scheduler
-    after steps), positions_scored, and per-layout metas.
+    after steps), positions_scored, per-layout metas, and rows (active rows when the run returned).
+    max_rounds > 0 stops the run after that many rounds, right after a compact: st and rows are then
+    the whole state, and run(st, rows, ...) continues it (its opening admission admits nothing new,
+    since the compact just before it stopped admitting on the same state).
     """
     assert mode in ("sync", "fdfo", "handback")
     trace = dict(steps=0, request_steps=0, idle_request_steps=0, rounds=0, positions_scored=0, metas=[], max_cost=0)
@@ -67,4 +70,7 @@ def run(st: dict, rows: int, L: int, mask_id: int, pad_id: int, dtype: str, budg
                        done=out["done"])
         trace["metas"].append(meta)
         rows, W = meta["rows"], meta["W"]
+        if max_rounds and trace["rounds"] >= max_rounds:
+            break
+    trace["rows"] = rows
     return trace

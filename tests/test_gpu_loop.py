@@ -349,3 +349,59 @@ def test_loop_phase_timing_brackets_every_call():
     assert runs[False][0] == runs[True][0]
     for k in ("row_req", "b", "state", "arena", "blk_mask"):
         assert np.array_equal(runs[False][1][k], runs[True][1][k]), k
+
+
+@pytest.mark.parametrize("mode", ["sync", "fdfo", "handback"])
+def test_checkpoint_resume_bit_identical(mode):
+    """A run stopped between two scheduler rounds, copied to the host with snapshot() and continued
+    by a fresh session from that copy, ends with the tables and accounting of a run that never
+    stopped."""
+    from confidence_block_unmasking_amd.driver import Session
+    w = configs.small(L=8, V=1000, n_act=4, n_q=14, K=3, seed=23, dtype="bf16", rows_cap=6, budget=200,
+                      p_range=(3, 24), sigma=1, umax=12)
+    fwd = gpu_forward(w)
+    whole = Session.from_workload(w)
+    full = dict(whole.run(mode, fwd))
+    ref = whole.host_table()
+    keys = ("steps", "request_steps", "idle_request_steps", "rounds", "positions_scored", "evicted", "admitted")
+    assert full["rounds"] >= 4, full
+    for k in (1, full["rounds"] // 2, full["rounds"] - 1):
+        first = Session.from_workload(w)
+        a = dict(first.run(mode, fwd, max_rounds=k))
+        assert a["rounds"] == k
+        snap = first.snapshot()
+        del first
+        second = Session.from_snapshot(snap)
+        b = dict(second.run(mode, fwd))
+        got = second.host_table()
+        for name in ("arena", "b", "state", "blk_mask", "row_req", "queue"):
+            assert np.array_equal(got[name], ref[name]), (mode, k, name)
+        for key in keys:
+            assert a[key] + b[key] == full[key], (mode, k, key, a[key], b[key], full[key])
+        print(f"{mode}: resumed after {k} of {full['rounds']} rounds", flush=True)
+
+
+def test_loop_metrics_unmasked_fallback_block_steps():
+    """Run metrics on the A/B/C example: constant logits never clear the threshold, so every
+    row-step with masks is a fallback that unmasks one slot, and block i takes exactly T_i steps.
+    On a seeded workload, every token of every block is unmasked exactly once over a whole run."""
+    import collections
+    T = [3, 8, 2]
+    for mode in ("sync", "fdfo"):
+        sess = _abc_session(T)
+        st = sess.run(mode, lambda s: s.logits.zero_(), metrics=True)
+        assert st["unmasked"] == sum(T), mode
+        assert st["fallback_row_steps"] == sum(T), mode
+        assert st["block_steps"] == dict(collections.Counter(T)), (mode, st["block_steps"])
+    from confidence_block_unmasking_amd.driver import Session
+    w = configs.small(L=8, V=1000, n_act=4, n_q=14, K=3, seed=23, dtype="bf16", rows_cap=6, budget=200,
+                      p_range=(3, 24), sigma=1, umax=12)
+    total = int(w.blk_mask.sum()) + int(((w.K - w.b - 1) * w.L).sum())
+    for mode in ("sync", "fdfo", "handback"):
+        st = Session.from_workload(w).run(mode, gpu_forward(w), metrics=True)
+        assert st["unmasked"] == total, (mode, st["unmasked"], total)
+        assert sum(st["block_steps"].values()) == int((w.K - w.b).sum()), mode
+        assert sum(k * v for k, v in st["block_steps"].items()) == st["request_steps"] - st["idle_request_steps"]
+        assert 0 < st["fallback_row_steps"] <= st["request_steps"] - st["idle_request_steps"]
+        print(f"{mode}: unmasked {st['unmasked']}, fallback row-steps {st['fallback_row_steps']}, "
+              f"block steps {sorted(st['block_steps'].items())}", flush=True)

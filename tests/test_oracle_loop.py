@@ -116,3 +116,29 @@ def test_fdfo_never_slower_in_steps_than_sync_for_one_batch():
     assert steps["sync"]["positions_scored"] == steps["fdfo"]["positions_scored"]
     assert steps["sync"]["steps"] == steps["fdfo"]["steps"]
     assert steps["fdfo"]["request_steps"] <= steps["sync"]["request_steps"]
+
+
+@pytest.mark.parametrize("mode", ["sync", "fdfo", "handback"])
+def test_resume_from_tables_continues_identically(mode):
+    """The request table, arena, block masks, row map and queue are the whole state between two
+    scheduler rounds: a run stopped after k rounds and continued from a copy of that state ends
+    with the same tables and the same accounting as a run that never stopped."""
+    w = configs.small(L=4, V=48, n_act=0, n_q=7, K=3, seed=5, dtype="bf16", sigma=1, umax=6)
+    st = _state(w)
+    st["row_req"] = np.full(w.n_req, -1, np.int64)
+    full = oloop.run(st, 0, w.L, w.mask_id, w.pad_id, w.dtype, 30, 3, mode, _gen(w))
+    keys = ("steps", "request_steps", "idle_request_steps", "rounds", "positions_scored")
+    for k in (1, 2, full["rounds"] - 1):
+        part = _state(w)
+        part["row_req"] = np.full(w.n_req, -1, np.int64)
+        first = oloop.run(part, 0, w.L, w.mask_id, w.pad_id, w.dtype, 30, 3, mode, _gen(w), max_rounds=k)
+        assert first["rounds"] == k
+        saved = {name: np.array(v, copy=True) for name, v in part.items()}
+        rest = oloop.run(saved, first["rows"], w.L, w.mask_id, w.pad_id, w.dtype, 30, 3, mode, _gen(w))
+        for name in ("arena", "b", "state", "blk_mask", "row_req", "queue"):
+            assert np.array_equal(saved[name], st[name]), (k, name)
+        for key in keys:
+            assert first[key] + rest[key] == full[key], (k, key)
+        m0, m1 = rest["metas"][0], first["metas"][-1]
+        assert (m0["rows"], m0["W"], m0["n_admitted"], m0["n_evicted"]) == (m1["rows"], m1["W"], 0, 0)
+        assert first["metas"] + rest["metas"][1:] == full["metas"]
