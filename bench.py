@@ -14,9 +14,10 @@ Reports masked positions scored per second over the timed region, the HBM roofli
 the scoring kernel (the dominant one) from HIP events on the launch stream, and the float64
 oracle's rate on the host cores (run first, before the GPU is touched).
 
-Other modes: --copy-calibration MIB runs only a plain device copy (for scaling the HBM byte
-counters); --record-traffic turns rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the stored traffic
-figure that later runs report.
+Other modes: --step large-fdfo times the same path on the largest single batch (256 requests at
+block 0, L=64, V=152064, every slot masked: 4.98 GB of logits per step); --copy-calibration MIB
+runs only a plain device copy (for scaling the HBM byte counters); --record-traffic turns
+rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the stored traffic figure that later runs report.
 """
 import argparse
 import ctypes
@@ -43,6 +44,13 @@ SCORE_SRC = [os.path.join(ROOT, "confidence_block_unmasking_amd", "csrc", f) for
 SCORE_KERNEL = "score_kernel"
 COPY_MIB = 256
 EV_EVERY = 8          # steps between two HIP-event samples of the scoring kernel
+DEFAULT_STEP = "dream-dynamic-step"
+STEP_WORKLOADS = {
+    "dream-dynamic-step": "Dream-shaped dynamic-threshold step: 64 requests, L=32, V=152064 bf16 logits, "
+                          "thresholds {0.5..0.9}, masked fraction U[0.1,1.0]; step = pack + score + decide + compact",
+    "large-fdfo": "first batch of the large FDFO run: 256 requests admitted at block 0, L=64, V=152064 bf16 "
+                  "logits, every slot masked (4.98 GB per step); step = pack + score + decide + compact",
+}
 
 
 def _sha(paths):
@@ -219,17 +227,20 @@ def run_gpu(args):
     from confidence_block_unmasking_amd.driver import Session
     from workload import configs, synth
 
-    w = configs.dream_step()
+    w = configs.make(args.step)
+    assert w.dtype == "bf16"
     sess = Session.from_workload(w)
     L, V = w.L, w.V
-    sess.compact(with_box=False)                       # initial layout: rows and box width
+    sess.compact(with_box=False)                       # initial layout (and admission): rows, box width
     rows, W = sess.rows, sess.W
-    M = int(w.blk_mask[w.row_req[:rows]].sum())
+    h = sess.host_table()
+    rq = h["row_req"][:rows].astype(np.int64)
+    M = int(h["blk_mask"][rq].sum())
     # logits buffers, generated on the device before timing (different seeds)
     bufs = []
-    rr = torch.from_numpy(w.row_req[:rows].astype(np.int32)).cuda()
-    bb = torch.from_numpy(w.b[w.row_req[:rows]].astype(np.int32)).cuda()
-    mm = torch.from_numpy(w.blk_mask[w.row_req[:rows]]).cuda()
+    rr = torch.from_numpy(rq.astype(np.int32)).cuda()
+    bb = torch.from_numpy(h["b"][rq].astype(np.int32)).cuda()
+    mm = torch.from_numpy(h["blk_mask"][rq]).cuda()
     for k in range(args.rotate):
         t = torch.empty((rows, L, V), dtype=torch.bfloat16, device="cuda")
         synth.logits_gpu(t, w.dtype, rows, L, V, rr, bb, mm, w.logit_seed + 7919 * k, w.sigma, w.umax)
@@ -366,13 +377,11 @@ def run_gpu(args):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "Dream-shaped dynamic-threshold step: 64 requests, L=32, V=152064 bf16 logits, "
-                               "thresholds {0.5..0.9}, masked fraction U[0.1,1.0]; step = pack + score + decide + "
-                               "compact",
+        "config": {"workload": STEP_WORKLOADS[args.step],
                    "rule": "threshold" if args.rule == "threshold" else f"quota, {args.steps_per_block} steps per block",
                    "vocab_shards": max(1, args.shards),
                    **({"features": "dllm_step_features after each decision"} if args.features else {}),
-                   "requests": w.rows, "block_len": L, "vocab": V, "logits_dtype": "bf16",
+                   "requests": rows, "block_len": L, "vocab": V, "logits_dtype": "bf16",
                    "masked_positions_per_step": M, "box_width": W, "logits_buffers": args.rotate},
         "logits_GBps": step_bytes * args.steps / elapsed / 1e9,
         "score_kernel_us": {"samples": int(kern_ms.size), "mean": float(kern_ms.mean()) * 1e3, "p10": float(np.percentile(kern_ms, 10)) * 1e3,
@@ -381,7 +390,8 @@ def run_gpu(args):
         **({"dllm_step_cold_us": cold_us} if cold_us else {}),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": stored_traffic(M) if args.shards <= 1 and args.rule == "threshold" else None},
+                     "traffic": (stored_traffic(M) if args.shards <= 1 and args.rule == "threshold"
+                                 and args.step == DEFAULT_STEP else None)},
         **({"timed_kernel": f"dllm_step_score_shard of shard 0 of {args.shards} (scoring + per-slot shard record)"}
            if args.shards > 1 else {}),
     }
@@ -427,6 +437,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--step", choices=tuple(STEP_WORKLOADS), default=DEFAULT_STEP,
+                    help="the batch one timed step processes (the default is the headline workload)")
     ap.add_argument("--rotate", type=int, default=4, help="logits buffers cycled through")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU work of the oracle baseline, in all")
     ap.add_argument("--rule", choices=("threshold", "quota"), default="threshold",
@@ -465,7 +477,8 @@ def main():
             raise SystemExit(f"--loop takes one of {', '.join(configs.LOOPS)}")
         print(json.dumps(run_loop(args.loop, args.mode)), flush=True)
         return
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)   # before the GPU is touched
+    # the oracle baseline is taken on the headline workload only, before the GPU is touched
+    cpu = None if args.no_cpu_baseline or args.step != DEFAULT_STEP else cpu_baseline(args.cpu_seconds)
     out = run_gpu(args)
     if cpu is not None:
         out["cpu_baseline"] = cpu
