@@ -58,37 +58,37 @@ def lib():
                                "(or __graft_entry__.build()); there is no fallback path")
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-        L.dllm_step.argtypes = [vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp,
+        L.dllm_step.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                 vp, vp, vp, sz, vp]
-        L.dllm_step.restype = ctypes.c_int
-        L.dllm_step_score.argtypes = [vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, vp, sz, vp]
-        L.dllm_step_score.restype = ctypes.c_int
-        L.dllm_step_decide.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+        L.dllm_step.restype = i32
+        L.dllm_step_score.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, vp, sz, vp]
+        L.dllm_step_score.restype = i32
+        L.dllm_step_decide.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, sz, vp]
-        L.dllm_step_decide.restype = ctypes.c_int
-        L.dllm_step_quota.argtypes = [vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp,
+        L.dllm_step_decide.restype = i32
+        L.dllm_step_quota.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp,
                                       vp, vp, vp, vp, sz, vp]
-        L.dllm_step_quota.restype = ctypes.c_int
-        L.dllm_step_decide_quota.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp,
+        L.dllm_step_quota.restype = i32
+        L.dllm_step_decide_quota.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp,
                                              vp, vp, vp, sz, vp]
-        L.dllm_step_decide_quota.restype = ctypes.c_int
+        L.dllm_step_decide_quota.restype = i32
         L.dllm_step_features.argtypes = [vp, i32, i32, vp, ctypes.POINTER(Reqs), vp, vp, vp, vp]
-        L.dllm_step_features.restype = ctypes.c_int
+        L.dllm_step_features.restype = i32
         L.dllm_shard_triples_bytes.argtypes = [i32, i32, i32]
         L.dllm_shard_triples_bytes.restype = sz
-        L.dllm_step_score_shard.argtypes = [vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, i32, i32, i32, vp, vp, sz,
+        L.dllm_step_score_shard.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, i32, i32, i32, vp, vp, sz,
                                             vp, vp]
-        L.dllm_step_score_shard.restype = ctypes.c_int
+        L.dllm_step_score_shard.restype = i32
         L.dllm_step_decide_shards.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                               vp]
-        L.dllm_step_decide_shards.restype = ctypes.c_int
-        L.dllm_step_workspace_bytes.argtypes = [i32, i32, i32, ctypes.c_int]
+        L.dllm_step_decide_shards.restype = i32
+        L.dllm_step_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.dllm_step_workspace_bytes.restype = sz
         L.dllm_pack.argtypes = [vp, i32, i32, i32, i32, vp, ctypes.POINTER(Reqs), vp, vp, vp, vp, vp, vp, vp, vp]
-        L.dllm_pack.restype = ctypes.c_int
+        L.dllm_pack.restype = i32
         L.dllm_compact.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, ctypes.POINTER(Reqs),
                                    ctypes.POINTER(Queue), i64, vp, vp]
-        L.dllm_compact.restype = ctypes.c_int
+        L.dllm_compact.restype = i32
         L.dllm_last_error.argtypes = []
         L.dllm_last_error.restype = ctypes.c_char_p
         _lib = L
