@@ -282,7 +282,10 @@ dllm_status dllm_pack(void *stream, int32_t rows, int32_t L, int32_t W, int32_t 
  * or all NULL; with all NULL only steps 3-5 run (the start of a run).  row_req: int32 [rows_cap],
  * entries >= rows ignored on entry.  meta: device dllm_meta.
  * Synchronous errors: null required pointer, rows < 0, rows > rows_cap, rows_cap > DLLM_MAX_ROWS,
- * L outside [1, DLLM_MAX_L], queue->cap outside [0, DLLM_MAX_QUEUE], box given with W < L.
+ * L outside [1, DLLM_MAX_L], queue->cap outside [0, DLLM_MAX_QUEUE], box given with W < L; and
+ * DLLM_ERR_CAPACITY when rows_cap * 21 + queue->cap * 9 + 16 bytes (the row map and the queue's
+ * prompt lengths, held in LDS) plus 4 KiB exceed the device's LDS per workgroup: on MI355X
+ * (160 KiB) 4096 rows leave room for a queue of 8190.
  * Device errors: a row holding an id out of range, not active, or with b outside [0, K) ->
  * DLLM_ERR_ARG (the row is dropped); a queue entry out of range, not queued, or with K < 1 ->
  * DLLM_ERR_ARG (nothing is admitted and the queue is left as it is); *queue->len outside

@@ -405,3 +405,39 @@ def test_loop_metrics_unmasked_fallback_block_steps():
         assert 0 < st["fallback_row_steps"] <= st["request_steps"] - st["idle_request_steps"]
         print(f"{mode}: unmasked {st['unmasked']}, fallback row-steps {st['fallback_row_steps']}, "
               f"block steps {sorted(st['block_steps'].items())}", flush=True)
+
+
+def test_compact_queue_capacity_at_the_lds_limit():
+    """dllm_compact holds its row map and the queue's prompt lengths in LDS: rows_cap * 21 +
+    cap * 9 + 16 bytes, plus 4 KiB, must fit one workgroup.  Beside the maximum row count, the
+    largest queue that fits is admitted (every row filled, the rest left queued in order); one
+    more entry is refused before anything is launched."""
+    from confidence_block_unmasking_amd import _lib, api
+    from confidence_block_unmasking_amd.driver import Session
+    lim = torch.cuda.get_device_properties(0).shared_memory_per_block
+    rows_cap = _lib.MAX_ROWS
+    cap_ok = min(_lib.MAX_QUEUE, (lim - 4096 - 16 - rows_cap * 21) // 9)
+    assert cap_ok > rows_cap, (lim, cap_ok)
+    print(f"LDS per workgroup {lim} B: queue capacity {cap_ok} beside {rows_cap} rows", flush=True)
+    w = configs.small(L=4, V=16, n_act=0, n_q=cap_ok, K=1, seed=3, rows_cap=rows_cap, p_range=(1, 8))
+    w.row_req = np.full(rows_cap, -1, np.int32)
+    sess = Session.from_workload(w)
+    m = sess.compact(with_box=False)
+    assert (m["rows"], m["n_admitted"], m["n_queued"]) == (rows_cap, rows_cap, cap_ok - rows_cap), m
+    h = sess.host_table()
+    rr = h["row_req"]
+    assert len(set(rr.tolist())) == rows_cap and rr.min() >= 0
+    assert np.array_equal(np.sort(np.flatnonzero(h["state"] == 1)), np.sort(rr))
+    left = h["queue"]
+    assert len(left) == cap_ok - rows_cap and np.all(h["state"][left] == 0)
+    # with no budget every candidate fits after the one before it, so admission takes the queue in
+    # its (p, id) order (the oracle's compact does the same on small queues): the first rows_cap
+    # entries hold the rows and the rest stay queued in order
+    assert np.array_equal(left, w.queue[rows_cap:])
+    assert np.array_equal(np.sort(rr), np.sort(w.queue[:rows_cap]))
+    if cap_ok < _lib.MAX_QUEUE:
+        big = api.DevQueue(np.arange(cap_ok + 1, dtype=np.int32) % cap_ok)
+        with pytest.raises(api.DllmError) as e:
+            api.dllm_compact(0, w.L, 0, w.mask_id, -1, sess.row_req, rows_cap, sess.reqs, big, 0, sess.meta,
+                             sess.status)
+        assert e.value.code == _lib.DLLM_ERR_CAPACITY
