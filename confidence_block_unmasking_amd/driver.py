@@ -59,6 +59,11 @@ class Session:
         self.status = torch.zeros(1, dtype=i32, device=device)
         self.meta = torch.zeros(32, dtype=u8, device=device)
         self.features_buf = torch.empty(n * api.N_FEATURES, dtype=f32, device=device)
+        # pinned host copies for the per-step read-back (done, new mask and status in one sync)
+        pin = str(device).startswith("cuda")
+        self._h_done = torch.empty(n, dtype=u8, pin_memory=pin)
+        self._h_mask = torch.empty(n * self.L, dtype=u8, pin_memory=pin)
+        self._h_status = torch.empty(1, dtype=i32, pin_memory=pin)
         self.logits = logits if logits is not None else torch.empty((n, self.L, self.V), dtype=dtype, device=device)
         self.W = 0
         self.stats = dict(steps=0, request_steps=0, positions_scored=0, compacts=0, packs=0, rounds=0,
@@ -80,6 +85,17 @@ class Session:
 
     def mask(self):
         return self.masks[self.cur][:self.rows * self.L].view(self.rows, self.L)
+
+    def _readback(self):
+        """done [rows] and the current mask [rows, L] on the host, and the status word: three
+        asynchronous copies into pinned memory and one synchronisation."""
+        n, nl = self.rows, self.rows * self.L
+        self._h_done[:n].copy_(self.done[:n], non_blocking=True)
+        self._h_mask[:nl].copy_(self.masks[self.cur][:nl], non_blocking=True)
+        self._h_status.copy_(self.status, non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        return (self._h_done[:n].numpy().copy(), self._h_mask[:nl].numpy().reshape(n, self.L).copy(),
+                int(self._h_status[0]))
 
     def check_status(self, where):
         s = int(self.status.item())
@@ -175,9 +191,9 @@ class Session:
                 self.stats["positions_scored"] += int(masked.sum())
                 self._timed("forward", timed, lambda: forward(self))
                 self.step(timed=timed)
-                done = self.done[:self.rows].cpu().numpy()
-                mask_host = self.mask().cpu().numpy()
-                self.check_status("dllm_step")
+                done, mask_host, st = self._readback()
+                if st != 0:
+                    raise api.DllmError(st, "dllm_step", "(device status)")
                 self.stats["steps"] += 1
                 unmasked = int(masked.sum()) - int((mask_host != 0).sum())
                 self.stats["unmasked"] += unmasked
