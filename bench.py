@@ -43,7 +43,7 @@ SCORE_SRC = [os.path.join(ROOT, "confidence_block_unmasking_amd", "csrc", f) for
             [os.path.join(ROOT, "include", "dllm.h")]
 SCORE_KERNEL = "score_kernel"
 COPY_MIB = 256
-EV_EVERY = 8          # steps between two HIP-event samples of the scoring kernel
+EV_EVERY = 16         # steps between two HIP-event timings of the scoring kernel
 DEFAULT_STEP = "dream-dynamic-step"
 STEP_WORKLOADS = {
     "dream-dynamic-step": "Dream-shaped dynamic-threshold step: 64 requests, L=32, V=152064 bf16 logits, "
@@ -223,7 +223,7 @@ def run_gpu(args):
     import numpy as np
     import torch
 
-    from confidence_block_unmasking_amd import _lib
+    from confidence_block_unmasking_amd import _lib, api
     from confidence_block_unmasking_amd.driver import Session
     from workload import configs, synth
 
@@ -292,11 +292,15 @@ def run_gpu(args):
         comp_args.append((stream, rows, L, W, w.mask_id, -1, P(box), P(mask_b), P(sess.done), P(c.row_req),
                           w.rows_cap, ctypes.byref(c.reqs), ctypes.byref(c.queue), w.budget, P(c.meta),
                           P(sess.status)))
-    # HIP events on the launch stream (torch's current stream), around the scoring kernel of every
-    # EV_EVERY-th step: an event record costs the stream a few microseconds, so bracketing every
-    # step would inflate the step time that `value` is computed from
+    # HIP events on the launch stream (torch's current stream) for the scoring kernel of every
+    # --ev-every-th step: timing costs the stream some microseconds, so timing every step would
+    # inflate the step time that `value` is computed from.  The events are bound to the kernel's own
+    # start and end (dllm_step_score_timed); the vocabulary-shard mode, which has no timed variant,
+    # records a pair around the first shard's call instead (that also holds the dispatch latency)
+    samples = [k for k in range(n_total) if k % args.ev_every == 0]
+    kev = {k: api.KernelEvents() for k in samples} if args.shards <= 1 else {}
     ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for k in range(n_total) if k % EV_EVERY == 0}
+          for k in samples} if args.shards > 1 else {}
 
     def one(k):
         rc = lib.dllm_pack(*pack_args[k])
@@ -310,10 +314,10 @@ def run_gpu(args):
                 e[1].record()
             for t in range(1, args.shards):
                 rc |= lib.dllm_step_score_shard(*sa[t])
+        elif k in kev:
+            rc |= lib.dllm_step_score_timed(*score_args[k % args.rotate], kev[k].start, kev[k].stop)
         else:
             rc |= lib.dllm_step_score(*score_args[k % args.rotate])
-            if e:
-                e[1].record()
         rc |= decide_fn(*decide_args)
         if args.features:
             rc |= lib.dllm_step_features(*feat_args[k])
@@ -359,7 +363,10 @@ def run_gpu(args):
                    "what": "dllm_step_score + dllm_step_decide between two HIP events, each launch after a "
                            "1 GiB write that evicts L2 and the Infinity Cache"}
         del flush
-    kern_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(args.warmup, n_total) if k in ev])
+    if kev:
+        kern_ms = np.array([kev[k].elapsed_ms() for k in range(args.warmup, n_total) if k in kev])
+    else:
+        kern_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(args.warmup, n_total) if k in ev])
     kern_s = float(kern_ms.mean()) / 1e3
     step_bytes = M * V * 2
     timed_bytes = step_bytes if args.shards <= 1 else M * (V // args.shards) * 2
@@ -384,9 +391,12 @@ def run_gpu(args):
                    "requests": rows, "block_len": L, "vocab": V, "logits_dtype": "bf16",
                    "masked_positions_per_step": M, "box_width": W, "logits_buffers": args.rotate},
         "logits_GBps": step_bytes * args.steps / elapsed / 1e9,
-        "score_kernel_us": {"samples": int(kern_ms.size), "mean": float(kern_ms.mean()) * 1e3, "p10": float(np.percentile(kern_ms, 10)) * 1e3,
+        "score_kernel_us": {"samples": int(kern_ms.size), "mean": float(kern_ms.mean()) * 1e3,
+                            "p10": float(np.percentile(kern_ms, 10)) * 1e3,
                             "p50": float(np.percentile(kern_ms, 50)) * 1e3,
-                            "p90": float(np.percentile(kern_ms, 90)) * 1e3},
+                            "p90": float(np.percentile(kern_ms, 90)) * 1e3,
+                            "what": ("HIP events bound to the kernel's start and end (dllm_step_score_timed)"
+                                     if kev else "HIP events recorded around the call")},
         **({"dllm_step_cold_us": cold_us} if cold_us else {}),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
@@ -440,6 +450,7 @@ def main():
     ap.add_argument("--step", choices=tuple(STEP_WORKLOADS), default=DEFAULT_STEP,
                     help="the batch one timed step processes (the default is the headline workload)")
     ap.add_argument("--rotate", type=int, default=4, help="logits buffers cycled through")
+    ap.add_argument("--ev-every", type=int, default=EV_EVERY, help="steps between two timings of the scoring kernel")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU work of the oracle baseline, in all")
     ap.add_argument("--rule", choices=("threshold", "quota"), default="threshold",
                     help="unmasking rule: LowConfidence threshold (default) or the fixed per-step quota")
@@ -463,6 +474,8 @@ def main():
         print(f"bench.py: the step runs on one GPU only (asked for --gpus {args.gpus}); its rows would shard "
               "across GPUs without any exchange, but no multi-GPU launcher is provided", file=sys.stderr)
         sys.exit(2)
+    if args.ev_every < 1 or args.ev_every > args.steps:
+        raise SystemExit("--ev-every must lie in [1, --steps], so that a timed step carries a timing")
     if args.record_traffic:
         from workload import configs
         w = configs.dream_step()

@@ -17,7 +17,7 @@ STATUS_NAMES = {0: "DLLM_OK", 1: "DLLM_ERR_ARG", 2: "DLLM_ERR_SHAPE", 3: "DLLM_E
 DLLM_FP32, DLLM_BF16 = 0, 1
 MAX_L, MAX_ROWS, MAX_POSITIONS, MAX_QUEUE = 1024, 4096, 262144, 8192
 
-EXPORTS = ("dllm_step", "dllm_step_score", "dllm_step_decide", "dllm_step_quota", "dllm_step_decide_quota",
+EXPORTS = ("dllm_step", "dllm_step_score", "dllm_step_score_timed", "dllm_step_decide", "dllm_step_quota", "dllm_step_decide_quota",
            "dllm_step_features", "dllm_step_score_shard", "dllm_step_decide_shards", "dllm_shard_triples_bytes",
            "dllm_step_workspace_bytes", "dllm_pack", "dllm_compact", "dllm_last_error")
 
@@ -63,6 +63,8 @@ def lib():
         L.dllm_step.restype = i32
         L.dllm_step_score.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, vp, sz, vp]
         L.dllm_step_score.restype = i32
+        L.dllm_step_score_timed.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, vp, sz, vp, vp, vp]
+        L.dllm_step_score_timed.restype = i32
         L.dllm_step_decide.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, sz, vp]
         L.dllm_step_decide.restype = i32
@@ -89,6 +91,14 @@ def lib():
         L.dllm_compact.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, ctypes.POINTER(Reqs),
                                    ctypes.POINTER(Queue), i64, vp, vp]
         L.dllm_compact.restype = i32
+        # the HIP runtime's event calls, reached through this library's own dependency (the same
+        # runtime torch uses), for the kernel-bound timing of dllm_step_score_timed
+        L.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+        L.hipEventSynchronize.argtypes = [vp]
+        L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        L.hipEventDestroy.argtypes = [vp]
+        for f in (L.hipEventCreate, L.hipEventSynchronize, L.hipEventElapsedTime, L.hipEventDestroy):
+            f.restype = ctypes.c_int
         L.dllm_last_error.argtypes = []
         L.dllm_last_error.restype = ctypes.c_char_p
         _lib = L

@@ -119,6 +119,46 @@ def dllm_step_score(logits, mask_in, workspace, status, rows=None, L=None, V=Non
     _lib.check(rc, "dllm_step_score")
 
 
+class KernelEvents:
+    """Two HIP events with timing enabled, for dllm_step_score_timed.  They are created through the
+    HIP runtime that libdllm.so and torch share; elapsed_ms() waits for the second one."""
+
+    def __init__(self):
+        hip = _lib.lib()
+        self._hip = hip
+        self.start, self.stop = ctypes.c_void_p(), ctypes.c_void_p()
+        for e in (self.start, self.stop):
+            if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+
+    def elapsed_ms(self) -> float:
+        if self._hip.hipEventSynchronize(self.stop) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.start, self.stop) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        for e in (getattr(self, "start", None), getattr(self, "stop", None)):
+            if e is not None and e.value:
+                self._hip.hipEventDestroy(e)
+
+
+def dllm_step_score_timed(logits, mask_in, workspace, status, events, rows=None, L=None, V=None, pos_stride=None,
+                          row_stride=None, stream=None):
+    """dllm_step_score with the scoring kernel's own start and end recorded into `events`
+    (a KernelEvents)."""
+    rows, L, V, pos_stride, row_stride = _logits_shape(logits, rows, L, V, pos_stride, row_stride)
+    _need(mask_in, torch.uint8, "mask_in", rows * L)
+    _need(workspace, torch.uint8, "workspace")
+    _need(status, torch.int32, "status", 1)
+    rc = _lib.lib().dllm_step_score_timed(_stream(stream), _ptr(logits), _DT[logits.dtype], pos_stride, row_stride,
+                                          rows, L, V, _ptr(mask_in), _ptr(workspace), workspace.numel(),
+                                          _ptr(status), events.start, events.stop)
+    _lib.check(rc, "dllm_step_score_timed")
+
+
 def dllm_step_decide(dtype, rows, L, V, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status,
                      p=None, b=None, conf=None, argmax=None, stream=None):
     """The deciding half of dllm_step, on the partials dllm_step_score left in `workspace`

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(StepParams P, int win) 
 }
 
 
-dllm_status launch_score(const StepParams &P, int32_t dtype, hipStream_t st) {
+dllm_status launch_score(const StepParams &P, int32_t dtype, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
     const int es = dtype == DLLM_BF16 ? 2 : 4;
     const int64_t S = (int64_t)P.rows * P.L;
     const int NC = P.NC;
@@ -186,12 +186,17 @@ dllm_status launch_score(const StepParams &P, int32_t dtype, hipStream_t st) {
     const int64_t per = (S * NC + grid - 1) / grid;
     const int win = (int)((per + NC - 1) / NC + 2);
     const size_t lds = (size_t)win * sizeof(int);
+    // with events: the same launch, the events taking the kernel's own start and end times
+    auto go = [&](auto kernel) {
+        if (ev_start) hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), lds, st, ev_start, ev_stop, 0, P, win);
+        else hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
+    };
     if (dtype == DLLM_BF16) {
-        if (aligned) hipLaunchKernelGGL((score_kernel<true, true>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
-        else hipLaunchKernelGGL((score_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
+        if (aligned) go(score_kernel<true, true>);
+        else go(score_kernel<true, false>);
     } else {
-        if (aligned) hipLaunchKernelGGL((score_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
-        else hipLaunchKernelGGL((score_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), lds, st, P, win);
+        if (aligned) go(score_kernel<false, true>);
+        else go(score_kernel<false, false>);
     }
     return check_hip(hipGetLastError(), "dllm_step score launch");
 }

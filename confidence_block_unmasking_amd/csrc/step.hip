@@ -157,6 +157,20 @@ extern "C" dllm_status dllm_step_score(void *stream, const void *logits, int32_t
     return launch_score(P, dtype, (hipStream_t)stream);
 }
 
+extern "C" dllm_status dllm_step_score_timed(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
+                                             int64_t row_stride, int32_t rows, int32_t L, int32_t V,
+                                             const uint8_t *mask_in, void *workspace, size_t workspace_bytes,
+                                             int32_t *status, void *start_event, void *stop_event) {
+    if (!start_event || !stop_event) return fail(DLLM_ERR_ARG, "dllm_step_score_timed: null event");
+    StepParams P{};
+    dllm_status rc = check_shape("dllm_step_score_timed", dtype, rows, L, V, workspace, P);
+    if (rc == DLLM_OK)
+        rc = check_score("dllm_step_score_timed", logits, dtype, pos_stride, row_stride, mask_in, status, P);
+    if (rc == DLLM_OK) rc = check_workspace("dllm_step_score_timed", dtype, workspace, workspace_bytes, P);
+    if (rc != DLLM_OK || rows == 0) return rc;
+    return launch_score(P, dtype, (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event);
+}
+
 extern "C" dllm_status dllm_step_decide(void *stream, int32_t dtype, int32_t rows, int32_t L, int32_t V,
                                         int32_t *input_ids, int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
                                         const float *threshold, const int32_t *p, const int32_t *b, float *conf,

@@ -3,6 +3,8 @@
 // scan used by its prologue, and the workspace shape.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace dllm {
@@ -320,7 +322,10 @@ inline bool shape_of(int32_t rows, int32_t L, int32_t V, int32_t dt, int &NV, in
 
 
 // Launchers (score.hip, decide.hip): enqueue the kernels for checked parameters.
-dllm_status launch_score(const StepParams &P, int32_t dtype, hipStream_t st);
+// With ev_start (and ev_stop) given, the scoring kernel is launched with the two events bound to
+// its own start and end.
+dllm_status launch_score(const StepParams &P, int32_t dtype, hipStream_t st, hipEvent_t ev_start = nullptr,
+                         hipEvent_t ev_stop = nullptr);
 // mode: kRuleThreshold / kRuleQuota apply the row's rule; kEmitTriples writes each masked slot's
 // merged (max, sum, global index) into P.triples at shard P.shard instead.
 constexpr int kRuleThreshold = 0, kRuleQuota = 1, kEmitTriples = 2;

@@ -154,6 +154,16 @@ size_t dllm_step_workspace_bytes(int32_t rows, int32_t L, int32_t V, int32_t dty
 dllm_status dllm_step_score(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
                             int64_t row_stride, int32_t rows, int32_t L, int32_t V, const uint8_t *mask_in,
                             void *workspace, size_t workspace_bytes, int32_t *status);
+/* dllm_step_score_timed — dllm_step_score with its scoring kernel's execution timed: the two
+ * events (hipEvent_t handles created with timing enabled, owned by the caller) take the start and
+ * the end of that kernel itself, so hipEventElapsedTime gives its duration without the dispatch
+ * latency that an event pair recorded around the call also holds.  Partials, status and errors as
+ * for dllm_step_score, plus DLLM_ERR_ARG for a null event.  With rows == 0 nothing is launched and
+ * the events are not recorded. */
+dllm_status dllm_step_score_timed(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
+                                  int64_t row_stride, int32_t rows, int32_t L, int32_t V,
+                                  const uint8_t *mask_in, void *workspace, size_t workspace_bytes,
+                                  int32_t *status, void *start_event, void *stop_event);
 dllm_status dllm_step_decide(void *stream, int32_t dtype, int32_t rows, int32_t L, int32_t V,
                              int32_t *input_ids, int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
                              const float *threshold, const int32_t *p, const int32_t *b, float *conf,

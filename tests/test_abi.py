@@ -109,6 +109,29 @@ def test_step_halves_reject_bad_arguments():
     assert decide(rows=0, ids=None) == _lib.DLLM_OK
 
 
+def test_timed_score_rejects_bad_arguments():
+    # the same checks as dllm_step_score, plus the two events; all refused before any launch
+    L = _lib.lib()
+    need = L.dllm_step_workspace_bytes(4, 32, 1024, 1)
+    f, ws, ev = FAKE, ctypes.c_void_p(0x10000), ctypes.c_void_p(0x3000)
+
+    def timed(**kw):
+        a = dict(logits=f, dtype=1, ps=1024, rs=32 * 1024, rows=4, L=32, V=1024, mask=f, ws=ws, n=need, status=f,
+                 e0=ev, e1=ev)
+        a.update(kw)
+        return L.dllm_step_score_timed(None, a["logits"], a["dtype"], a["ps"], a["rs"], a["rows"], a["L"], a["V"],
+                                       a["mask"], a["ws"], a["n"], a["status"], a["e0"], a["e1"])
+    assert timed(e0=None) == _lib.DLLM_ERR_ARG
+    assert timed(e1=None) == _lib.DLLM_ERR_ARG
+    assert "event" in _lib.last_error()
+    assert timed(dtype=5) == _lib.DLLM_ERR_DTYPE
+    assert timed(logits=None) == _lib.DLLM_ERR_ARG
+    assert timed(ps=100) == _lib.DLLM_ERR_ARG
+    assert timed(n=need - 16) == _lib.DLLM_ERR_ARG
+    assert timed(L=0) == _lib.DLLM_ERR_SHAPE
+    assert timed(rows=0, logits=None, mask=None) == _lib.DLLM_OK
+
+
 def test_quota_rejects_bad_arguments():
     L = _lib.lib()
     need = L.dllm_step_workspace_bytes(4, 32, 1024, 1)

@@ -245,6 +245,21 @@ def test_step_halves_equal_step():
              conf=conf.cpu().numpy(), argmax=arg.cpu().numpy())
     for k in b:
         assert np.array_equal(a[k], b[k]), k
+    # the kernel-bound timed launch leaves the same partials: the same decisions again
+    ids.copy_(torch.from_numpy(pk["box_ids"].astype(np.int32)))
+    ws.fill_(0xA5)
+    ev = api.KernelEvents()
+    api.dllm_step_score_timed(lg, mask, ws, status, ev)
+    api.dllm_step_decide(torch.bfloat16, rows, L, V, ids, mask, mout, tau, done, acc, ws, status, conf=conf,
+                         argmax=arg)
+    ms = ev.elapsed_ms()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert 0.0 < ms < 1000.0
+    c = dict(ids=ids.cpu().numpy(), mask=mout.cpu().numpy(), done=done.cpu().numpy(), accept=acc.cpu().numpy(),
+             conf=conf.cpu().numpy(), argmax=arg.cpu().numpy())
+    for k in c:
+        assert np.array_equal(a[k], c[k]), k
 
 
 def test_step_in_place_mask_update():
