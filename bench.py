@@ -297,7 +297,16 @@ def run_gpu(args):
     # inflate the step time that `value` is computed from.  The events are bound to the kernel's own
     # start and end (dllm_step_score_timed); the vocabulary-shard mode, which has no timed variant,
     # records a pair around the first shard's call instead (that also holds the dispatch latency)
-    samples = [k for k in range(n_total) if k % args.ev_every == 0]
+    # the sampled steps cycle through the logits buffers (step k reads buffer k % rotate), so that
+    # every buffer is timed, not only the one that a stride dividing `rotate` would always land on
+    def _sample(i):
+        if args.rotate > args.ev_every:
+            return i * args.ev_every
+        return i * args.ev_every + (i % args.rotate - i * args.ev_every) % args.rotate   # buffer i % rotate
+    samples = [_sample(i) for i in range(n_total // args.ev_every + 1)]
+    samples = [k for k in samples if k < n_total]
+    if not any(k >= args.warmup for k in samples):
+        raise SystemExit("no timed step carries a timing of the scoring kernel: lower --ev-every")
     kev = {k: api.KernelEvents() for k in samples} if args.shards <= 1 else {}
     ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for k in samples} if args.shards > 1 else {}
@@ -363,10 +372,14 @@ def run_gpu(args):
                    "what": "dllm_step_score + dllm_step_decide between two HIP events, each launch after a "
                            "1 GiB write that evicts L2 and the Infinity Cache"}
         del flush
+    timed_k = [k for k in samples if k >= args.warmup]
     if kev:
-        kern_ms = np.array([kev[k].elapsed_ms() for k in range(args.warmup, n_total) if k in kev])
+        kern_ms = np.array([kev[k].elapsed_ms() for k in timed_k])
     else:
-        kern_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(args.warmup, n_total) if k in ev])
+        kern_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in timed_k])
+    by_buf = {}
+    for k, t in zip(timed_k, kern_ms):
+        by_buf.setdefault(k % args.rotate, []).append(float(t) * 1e3)
     kern_s = float(kern_ms.mean()) / 1e3
     step_bytes = M * V * 2
     timed_bytes = step_bytes if args.shards <= 1 else M * (V // args.shards) * 2
@@ -395,6 +408,8 @@ def run_gpu(args):
                             "p10": float(np.percentile(kern_ms, 10)) * 1e3,
                             "p50": float(np.percentile(kern_ms, 50)) * 1e3,
                             "p90": float(np.percentile(kern_ms, 90)) * 1e3,
+                            "by_logits_buffer": [round(float(np.mean(by_buf[b])), 2) if b in by_buf else None
+                                                 for b in range(args.rotate)],
                             "what": ("HIP events bound to the kernel's start and end (dllm_step_score_timed)"
                                      if kev else "HIP events recorded around the call")},
         **({"dllm_step_cold_us": cold_us} if cold_us else {}),
