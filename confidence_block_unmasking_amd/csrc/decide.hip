@@ -40,10 +40,12 @@ __device__ __forceinline__ int quota_for_remaining(int L, int S, int m) {
 // chunks, a fixed DPP tree, then blocks of 64 chunks in order), then the row's rule: LowConfidence
 // (QUOTA false) or the fixed per-step quota (QUOTA true: the k most confident masked slots, k from
 // quota_for_remaining, ties to the lowest j).
-// Each wave loads the partials and mask bytes of kGroup slots before reducing any of them, so a
-// row costs about one memory round trip; partials of unmasked slots are loaded but never used.
+// Each wave loads the partials and mask bytes of G slots before reducing any of them, so a row of
+// up to kDecideWaves*G slots costs about one memory round trip; partials of unmasked slots are
+// loaded but never used.  G is the smallest of 4 and 8 that covers the row in one pass (the merges
+// a wave runs one after the other are the rest of the kernel's time).
 // A row's mask bytes are read before any of its outputs is written, so mask_out may be mask_in.
-template <int MODE>
+template <int MODE, int G>
 __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
     constexpr bool QUOTA = MODE == kRuleQuota;
     extern __shared__ float s_conf[];           // [L]
@@ -63,23 +65,23 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
     // (no rule, and no rule inputs, when emitting shard results)
     const int32_t *rin = lane == 1 ? P.p : lane == 2 ? P.b : (const int32_t *)P.tau;
     const int32_t rule_in = MODE == kEmitTriples ? 0 : rin[row];
-    for (int g0 = wave; g0 < L; g0 += kDecideWaves * kGroup) {
-        // slots g0, g0 + 4, ..., g0 + 4*(kGroup-1) of this row; addresses are clamped into the
-        // row so that every load is unconditional and they all go out together
-        float Mr[kGroup], Sr[kGroup];
-        int vr[kGroup];
-        const int jm = g0 + (lane & (kGroup - 1)) * kDecideWaves;   // lane s loads slot s's mask byte
+    for (int g0 = wave; g0 < L; g0 += kDecideWaves * G) {
+        // slots g0, g0 + kDecideWaves, ..., g0 + kDecideWaves*(G-1) of this row; addresses are
+        // clamped into the row so that every load is unconditional and they all go out together
+        float Mr[G], Sr[G];
+        int vr[G];
+        const int jm = g0 + (lane & (G - 1)) * kDecideWaves;        // lane s loads slot s's mask byte
         const uint32_t mv = mrow[min(jm, L - 1)];
         uint32_t gm = 0;                                            // bit s: slot s is masked
         for (int base = 0; base < NC; base += 64) {
-            float4 t[kGroup];
+            float4 t[G];
             const bool in = base + lane < NC;
             const int cl = min(base + lane, NC - 1);
 #pragma unroll
-            for (int s = 0; s < kGroup; ++s) t[s] = prow[(int64_t)min(g0 + s * kDecideWaves, L - 1) * NC + cl];
-            if (base == 0) gm = (uint32_t)__ballot(lane < kGroup && jm < L && mv != 0) & ((1u << kGroup) - 1);
+            for (int s = 0; s < G; ++s) t[s] = prow[(int64_t)min(g0 + s * kDecideWaves, L - 1) * NC + cl];
+            if (base == 0) gm = (uint32_t)__ballot(lane < G && jm < L && mv != 0) & ((1u << G) - 1);
 #pragma unroll
-            for (int s = 0; s < kGroup; ++s) {
+            for (int s = 0; s < G; ++s) {
                 float Mb, Sb;
                 int vb;
                 merge_lanes(t[s], in && ((gm >> s) & 1), Mb, Sb, vb);
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
             // one shard's result per masked slot, its index made global
             if (lane == 0) {
 #pragma unroll
-                for (int s = 0; s < kGroup; ++s) {
+                for (int s = 0; s < G; ++s) {
                     const int j = g0 + s * kDecideWaves;
                     if (j < L && ((gm >> s) & 1))
                         P.triples[((int64_t)row * L + j) * P.n_shards + P.shard] =
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
         }
         if (lane == 0) {
 #pragma unroll
-            for (int s = 0; s < kGroup; ++s) {
+            for (int s = 0; s < G; ++s) {
                 const int j = g0 + s * kDecideWaves;
                 if (j < L) {
                     s_mask[j] = (gm >> s) & 1;
@@ -204,12 +206,18 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
 }
 
 
-dllm_status launch_decide(const StepParams &P, hipStream_t st, int mode) {
+template <int G>
+void launch_decide_g(const StepParams &P, hipStream_t st, int mode) {
     const size_t lds = (size_t)P.L * 10 + 16;
     const dim3 grid((unsigned)P.rows), block(kDecideThreads);
-    if (mode == kRuleQuota) hipLaunchKernelGGL(decide_kernel<kRuleQuota>, grid, block, lds, st, P);
-    else if (mode == kEmitTriples) hipLaunchKernelGGL(decide_kernel<kEmitTriples>, grid, block, lds, st, P);
-    else hipLaunchKernelGGL(decide_kernel<kRuleThreshold>, grid, block, lds, st, P);
+    if (mode == kRuleQuota) hipLaunchKernelGGL((decide_kernel<kRuleQuota, G>), grid, block, lds, st, P);
+    else if (mode == kEmitTriples) hipLaunchKernelGGL((decide_kernel<kEmitTriples, G>), grid, block, lds, st, P);
+    else hipLaunchKernelGGL((decide_kernel<kRuleThreshold, G>), grid, block, lds, st, P);
+}
+
+dllm_status launch_decide(const StepParams &P, hipStream_t st, int mode) {
+    if (P.L <= kDecideWaves * 4) launch_decide_g<4>(P, st, mode);
+    else launch_decide_g<8>(P, st, mode);
     return check_hip(hipGetLastError(), "dllm_step decide launch");
 }
 
