@@ -11,6 +11,9 @@
 
 namespace dllm {
 
+constexpr int kDecideThreads = 512;           // one workgroup per row: 8 waves
+constexpr int kDecideWaves = kDecideThreads / 64;
+
 // Merge of one slot's partials for chunks [base, base + 64) held one per lane: max over lanes,
 // lowest element index at that max, sum rescaled to that max.  A fixed network (reproducible).
 __device__ __forceinline__ void merge_lanes(const float4 &t, bool valid, float &Mb, float &Sb, int &vb) {

@@ -25,8 +25,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kVPL = DLLM_STEP_VPL;           // 16-byte vectors per lane per chunk
 constexpr int kCH = 64 * kVPL;                // vectors per chunk
 constexpr int kTile = kThreads * 16;          // mask bytes per prologue pass (16 per thread)
-constexpr int kDecideThreads = 512;
-constexpr int kDecideWaves = kDecideThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct StepParams {
