@@ -71,6 +71,29 @@ def test_quota_parity_random(dtype, rows, L, V, S):
         assert np.array_equal(g[k], h[k]), k
 
 
+@pytest.mark.parametrize("case", range(32))
+def test_quota_random_sweep(case):
+    # seeded random shapes, dtypes, mask densities and steps per block (including S > L and S = 1),
+    # through both the one-call step and its halves
+    rng = np.random.default_rng(7000 + case)
+    dtype = str(rng.choice(["fp32", "bf16"]))
+    rows = int(rng.integers(1, 17))
+    L = int(rng.choice([1, 3, 8, 16, 32, 33, 64, 65, 100]))
+    V = int(rng.integers(1, 5000))
+    V = max(1, min(V, 2_000_000 // (rows * L)))
+    S = int(rng.choice([1, 2, 5, 8, 16, 32, 64, 200]))
+    logits, ids, mask, _ = _rand_case(rng, rows, L, V, dtype, p_mask=float(rng.random()))
+    if rng.random() < 0.3:
+        mask[int(rng.integers(0, rows))] = 1
+    if rng.random() < 0.3:
+        mask[int(rng.integers(0, rows))] = 0
+    halves = bool(rng.random() < 0.5)
+    print(f"quota sweep case {case}: rows={rows} L={L} V={V} S={S} {dtype} halves={halves}", flush=True)
+    g = gpu_quota(logits, dtype, ids, mask, S, halves=halves)
+    assert g["status"] == 0
+    check_quota_step(logits, dtype, ids, mask, S, g)
+
+
 @pytest.mark.parametrize("L,S", [(32, 32), (32, 10), (7, 3), (64, 32), (5, 8), (40, 1), (65, 9), (100, 7)])
 def test_quota_count_for_every_masked_count(L, S):
     # row m has m masked slots: it unmasks exactly quota_for_remaining(L, S, m)

@@ -160,6 +160,41 @@ def test_step_shapes_and_ragged_tails(dtype, rows, L, V):
     check_step(logits, dtype, ids, mask, tau, g)
 
 
+@pytest.mark.parametrize("case", range(64))
+def test_step_random_sweep(case):
+    # seeded random cases: shape, dtype, strides and offset, mask density, thresholds at the ends of
+    # their range, in-place masks, a misaligned mask, p/b given or not; all against the oracle
+    rng = np.random.default_rng(9000 + case)
+    dtype = str(rng.choice(["fp32", "bf16"]))
+    rows = int(rng.integers(1, 25))
+    L = int(rng.choice([1, 2, 7, 16, 31, 32, 33, 64, 65, 100]))
+    V = int(rng.integers(1, 6000))
+    if rng.random() < 0.4:
+        V = max(8, V - V % 8)                   # whole 16-byte vectors: the vector path
+    V = max(1, min(V, 3_000_000 // (rows * L)))
+    logits, ids, mask, tau = _rand_case(rng, rows, L, V, dtype, p_mask=float(rng.random()))
+    if rng.random() < 0.3:
+        mask[int(rng.integers(0, rows))] = 0    # a row with nothing masked
+    if rng.random() < 0.3:
+        mask[int(rng.integers(0, rows))] = 1    # a fully masked row
+    tau = rng.choice([0.0, 0.2, 0.5, 0.9, 0.999, 1.0], rows).astype(np.float32)
+    kw = {}
+    if rng.random() < 0.5:
+        ps = V + int(rng.integers(0, 9))
+        kw = dict(pos_stride=ps, row_stride=L * ps + int(rng.integers(0, 9)), offset=int(rng.integers(0, 9)))
+    in_place = bool(rng.random() < 0.3)
+    moff = int(rng.integers(1, 16)) if rng.random() < 0.3 else 0
+    pb = {}
+    if rng.random() < 0.5:
+        W = ids.shape[1]
+        pb = dict(p=rng.integers(0, W - L + 1, rows).astype(np.int32), b=np.zeros(rows, np.int32))
+    print(f"sweep case {case}: rows={rows} L={L} V={V} {dtype} {kw} in_place={in_place} mask_offset={moff} "
+          f"pb={bool(pb)}", flush=True)
+    g = gpu_step(logits, dtype, ids, mask.copy(), tau, in_place=in_place, mask_offset=moff, **kw, **pb)
+    assert g["status"] == 0
+    check_step(logits, dtype, ids, mask, tau, g, **pb)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_step_strided_and_unaligned(dtype):
     rng = np.random.default_rng(17)
