@@ -182,6 +182,29 @@ def test_pack_compact_parity_random_small():
         lockstep_run(w, full_score_max=10**9, label=f"small{seed}")
 
 
+@pytest.mark.parametrize("case", range(16))
+def test_loop_random_sweep(case):
+    """Seeded random small runs in lockstep with the oracle: block length, vocabulary, queue length,
+    blocks per request, row capacity, budget (none, or tight but always admitting one request), sync
+    or FDFO, an end-of-sequence id on some."""
+    rng = np.random.default_rng(5000 + case)
+    L = int(rng.choice([1, 2, 3, 5, 8, 16, 32, 33]))
+    V = int(rng.integers(2, 300))
+    K = int(rng.integers(1, 6))
+    n_q = int(rng.integers(1, 41))
+    cap = int(rng.integers(1, 25))
+    pmax = int(rng.integers(1, 40))
+    budget = 0 if rng.random() < 0.4 else int((pmax + K * L) * rng.uniform(1.0, 6.0))
+    mode = str(rng.choice(["sync", "fdfo"]))
+    eos = int(rng.integers(0, V)) if rng.random() < 0.3 else -1
+    w = configs.small(L=L, V=V, n_act=0, n_q=n_q, K=K, seed=600 + case, dtype=str(rng.choice(["fp32", "bf16"])),
+                      budget=budget, rows_cap=cap, p_range=(1, pmax), mode=mode)
+    w.row_req = np.full(cap, -1, np.int32)
+    print(f"loop sweep case {case}: L={L} V={V} K={K} queue={n_q} cap={cap} p<={pmax} budget={budget} {mode} "
+          f"eos={eos}", flush=True)
+    lockstep_run(w, full_score_max=10**9, label=f"sweep{case}", eos_id=eos)
+
+
 def test_loop_at_the_row_limit():
     """Every row of a DLLM_MAX_ROWS-row box active, then a refill from the queue: step, pack and
     compact against the oracle at the largest box the library accepts."""
