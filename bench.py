@@ -85,23 +85,47 @@ def _cpu_worker(args):
                 return slots, time.perf_counter() - t0
 
 
-def cpu_baseline(cpu_seconds):
-    """The oracle's step on the same configuration, rows spread over a pool of host processes
-    (one thread each), for about `cpu_seconds` of CPU work in all.  Logits generation excluded."""
+def _first_batch(w):
+    """The workload's first batch as the oracle lays it out: admission by the oracle's compact when
+    the workload starts with an empty box, then the oracle's pack.  Returns (row_req, rows, W, pack)."""
     import numpy as np
 
+    from oracle import compact as ocompact
     from oracle import pack as opack
+    rows = w.rows
+    row_req = w.row_req
+    if rows == 0:
+        st = dict(p=w.p.astype(np.int64), K=w.K.astype(np.int64), b=w.b.astype(np.int64),
+                  state=w.state.astype(np.int64), threshold=w.threshold.copy(), arena_off=w.arena_off.copy(),
+                  arena=w.arena.astype(np.int64), blk_mask=w.blk_mask.copy(), row_req=w.row_req.astype(np.int64),
+                  queue=w.queue.astype(np.int64))
+        m = ocompact.compact(st, 0, w.L, 0, w.mask_id, -1, w.budget, w.rows_cap)
+        rows, row_req = m["rows"], st["row_req"]
+        p, b, thr, off, arena, blk = st["p"], st["b"], st["threshold"], st["arena_off"], st["arena"], st["blk_mask"]
+    else:
+        p, b, thr, off, arena, blk = w.p, w.b, w.threshold, w.arena_off, w.arena, w.blk_mask
+    W = opack.box_width(row_req, rows, p, b, w.L)
+    pk = opack.pack(row_req, rows, w.L, W, w.pad_id, p, b, thr, off, arena, blk)
+    return row_req, rows, W, pk
+
+
+def cpu_baseline(cpu_seconds, name=DEFAULT_STEP, max_logit_bytes=1 << 30):
+    """The oracle's step on the first batch of workload `name` (the headline step by default), rows
+    spread over a pool of host processes (one thread each), for about `cpu_seconds` of CPU work in
+    all.  At most `max_logit_bytes` of logits are generated (the first rows of the batch).  Logits
+    generation excluded."""
     from workload import configs, synth
-    w = configs.dream_step()
-    W = opack.box_width(w.row_req, w.rows, w.p, w.b, w.L)
-    pk = opack.pack(w.row_req, w.rows, w.L, W, w.pad_id, w.p, w.b, w.threshold, w.arena_off, w.arena, w.blk_mask)
-    _CPU.update(logits=synth.logits_cpu(w.rows, w.L, w.V, w.dtype, w.row_req, pk["b"], pk["mask"], w.logit_seed,
-                                        w.sigma, w.umax),
-                dtype=w.dtype, ids=pk["box_ids"], mask=pk["mask"], tau=pk["threshold"],
-                nmask=[int(x) for x in pk["mask"].sum(1)])
-    n = max(1, min(16, os.cpu_count() or 1))
+    w = configs.make(name)
+    row_req, rows, W, pk = _first_batch(w)
+    rows_s = max(1, min(rows, max_logit_bytes // (w.L * w.V * w.elem_bytes)))
+    mask = pk["mask"][:rows_s]
+    _CPU.update(logits=synth.logits_cpu(rows_s, w.L, w.V, w.dtype, row_req[:rows_s], pk["b"][:rows_s], mask,
+                                        w.logit_seed, w.sigma, w.umax),
+                dtype=w.dtype, ids=pk["box_ids"][:rows_s], mask=mask, tau=pk["threshold"][:rows_s],
+                nmask=[int(x) for x in mask.sum(1)])
+    n = max(1, min(16, os.cpu_count() or 1, rows_s))
     per = max(1.0, cpu_seconds / n)
-    parts = [list(range(k, w.rows, n)) for k in range(n)]
+    parts = [list(range(k, rows_s, n)) for k in range(n)]
     os.environ["OMP_NUM_THREADS"] = "1"
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(n) as pool:
@@ -109,15 +133,18 @@ def cpu_baseline(cpu_seconds):
     wall = time.perf_counter() - t0
     slots = sum(s for s, _ in res)
     busy = max(t for _, t in res)
-    # the same oracle on one core, over every row in turn
+    # the same oracle on one core, over every sampled row in turn
     one_secs = max(1.0, cpu_seconds / 4)
-    slots1, busy1 = _cpu_worker((list(range(w.rows)), one_secs))
+    slots1, busy1 = _cpu_worker((list(range(rows_s)), one_secs))
     _CPU.clear()
     value = slots / busy
+    batch = "first batch" if name in configs.LOOPS else "step"
+    if rows_s < rows:
+        batch += f" ({rows_s} of its {rows} rows)"
     return {"value": value, "unit": "masked positions/s", "cores": len(res), "kind": "oracle",
-            "sample": f"{slots} masked-slot scorings of the same 64-row step (rows round-robin over {len(res)} "
-                      f"processes, one thread each, {per:.1f} s each, repeated passes; {wall:.1f} s wall); "
-                      "numpy float64; logits generation excluded",
+            "sample": f"{slots} masked-slot scorings of the {batch}, L={w.L}, V={w.V} {w.dtype} (rows round-robin "
+                      f"over {len(res)} processes, one thread each, {per:.1f} s each, repeated passes; {wall:.1f} s "
+                      "wall); numpy float64; logits generation excluded",
             "logits_GBps_equiv": value * w.V * w.elem_bytes / 1e9,
             "one_core": {"value": slots1 / busy1, "sample": f"{slots1} masked-slot scorings in {busy1:.1f} s, one "
                                                              "process"}}
@@ -503,10 +530,17 @@ def main():
         from workload import configs
         if args.loop not in configs.LOOPS:
             raise SystemExit(f"--loop takes one of {', '.join(configs.LOOPS)}")
-        print(json.dumps(run_loop(args.loop, args.mode)), flush=True)
+        cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, args.loop)
+        out = run_loop(args.loop, args.mode)
+        if cpu is not None:
+            cpu["estimated_loop_s"] = out["positions_scored"] / cpu["value"]
+            cpu["estimate"] = ("the loop's masked positions scored divided by the sampled rate: the oracle's "
+                               "scoring alone, on the same host processes")
+            out["cpu_baseline"] = cpu
+        print(json.dumps(out), flush=True)
         return
     # the oracle baseline is taken on the headline workload only, before the GPU is touched
-    cpu = None if args.no_cpu_baseline or args.step != DEFAULT_STEP else cpu_baseline(args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline or args.step != DEFAULT_STEP else cpu_baseline(args.cpu_seconds, args.step)
     out = run_gpu(args)
     if cpu is not None:
         out["cpu_baseline"] = cpu

@@ -82,3 +82,16 @@ def test_loop_names_are_checked():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--loop", "no-such-workload"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0 and "llada-sync" in (r.stderr + r.stdout)
+
+
+def test_oracle_baseline_batches(bench):
+    # the oracle's timed sample is the workload's own first batch: the headline step's 64 rows as
+    # packed, and for the large run the 256 requests the admission takes from the empty box first
+    from workload import configs
+    _, rows, W, pk = bench._first_batch(configs.make("dream-dynamic-step"))
+    assert rows == 64 and int(pk["mask"].sum()) == 1005 and pk["box_ids"].shape == (64, W)
+    w = configs.make("large-fdfo")
+    assert w.rows == 0
+    rr, rows, W, pk = bench._first_batch(w)
+    assert rows == 256 and pk["mask"].shape == (256, 64) and bool(pk["mask"].all())
+    assert len(set(int(q) for q in rr[:rows])) == rows
