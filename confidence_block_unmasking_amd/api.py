@@ -25,6 +25,19 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _launch(fn, args, where, events, stream):
+    """Call fn(*args) and check its status; with `events` (two timing events), they are recorded on
+    the launch stream right before and right after the call, after every argument is marshalled."""
+    if events is not None:
+        s = torch.cuda.current_stream() if stream is None else stream
+        events[0].record(s)
+        rc = fn(*args)
+        events[1].record(s)
+    else:
+        rc = fn(*args)
+    _lib.check(rc, where)
+
+
 def _need(t, dtype, name, numel=None):
     if t is None:
         raise ValueError(f"{name} is required")
@@ -91,20 +104,20 @@ def _decide_args(rows, L, input_ids, mask_in, mask_out, threshold, done, accept_
 
 def dllm_step(logits, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status,
               p=None, b=None, conf=None, argmax=None, rows=None, L=None, V=None, pos_stride=None,
-              row_stride=None, stream=None):
+              row_stride=None, stream=None, events=None):
     """One LowConfidence denoise step (see include/dllm.h).
 
     logits: [rows, L, V] bf16/fp32 device tensor, or any tensor whose storage holds element
-    (r, j, v) at r*row_stride + j*pos_stride + v when the strides are given.
+    (r, j, v) at r*row_stride + j*pos_stride + v when the strides are given.  events: optional
+    pair of timing events recorded right around the library call.
     """
     rows, L, V, pos_stride, row_stride = _logits_shape(logits, rows, L, V, pos_stride, row_stride)
     W = _decide_args(rows, L, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status, p, b,
                      conf, argmax)
-    rc = _lib.lib().dllm_step(_stream(stream), _ptr(logits), _DT[logits.dtype], pos_stride, row_stride, rows, L, V,
-                              _ptr(input_ids), W, _ptr(mask_in), _ptr(mask_out), _ptr(threshold), _ptr(p), _ptr(b),
-                              _ptr(conf), _ptr(argmax), _ptr(done), _ptr(accept_len), _ptr(workspace),
-                              workspace.numel(), _ptr(status))
-    _lib.check(rc, "dllm_step")
+    args = (_stream(stream), _ptr(logits), _DT[logits.dtype], pos_stride, row_stride, rows, L, V, _ptr(input_ids), W,
+            _ptr(mask_in), _ptr(mask_out), _ptr(threshold), _ptr(p), _ptr(b), _ptr(conf), _ptr(argmax), _ptr(done),
+            _ptr(accept_len), _ptr(workspace), workspace.numel(), _ptr(status))
+    _launch(_lib.lib().dllm_step, args, "dllm_step", events, stream)
 
 
 def dllm_step_score(logits, mask_in, workspace, status, rows=None, L=None, V=None, pos_stride=None,
@@ -290,8 +303,9 @@ class DevQueue:
 
 
 def dllm_pack(rows, L, W, pad_id, row_req, reqs: ReqTable, box_ids, mask, threshold, p, b, status,
-              box_valid=None, box_pos=None, stream=None):
-    """Gather the left-padded box for rows [0, rows) (see include/dllm.h)."""
+              box_valid=None, box_pos=None, stream=None, events=None):
+    """Gather the left-padded box for rows [0, rows) (see include/dllm.h).  events: optional pair
+    of timing events recorded right around the library call."""
     if rows > 0:
         _need(row_req, torch.int32, "row_req", rows)
         _need(box_ids, torch.int32, "box_ids", rows * W)
@@ -305,16 +319,16 @@ def dllm_pack(rows, L, W, pad_id, row_req, reqs: ReqTable, box_ids, mask, thresh
         if box_pos is not None:
             _need(box_pos, torch.int32, "box_pos", rows * W)
     st = reqs.struct()
-    rc = _lib.lib().dllm_pack(_stream(stream), rows, L, W, pad_id, _ptr(row_req), ctypes.byref(st), _ptr(box_ids),
-                              _ptr(box_valid), _ptr(box_pos), _ptr(mask), _ptr(threshold), _ptr(p), _ptr(b),
-                              _ptr(status))
-    _lib.check(rc, "dllm_pack")
+    args = (_stream(stream), rows, L, W, pad_id, _ptr(row_req), ctypes.byref(st), _ptr(box_ids), _ptr(box_valid),
+            _ptr(box_pos), _ptr(mask), _ptr(threshold), _ptr(p), _ptr(b), _ptr(status))
+    _launch(_lib.lib().dllm_pack, args, "dllm_pack", events, stream)
 
 
 def dllm_compact(rows, L, W, mask_id, eos_id, row_req, rows_cap, reqs: ReqTable, queue: DevQueue, budget, meta,
-                 status, box_ids=None, mask=None, done=None, stream=None):
+                 status, box_ids=None, mask=None, done=None, stream=None, events=None):
     """Commit finished blocks, evict, refill under the token budget (see include/dllm.h).
-    meta: device uint8 tensor of 32 bytes (a dllm_meta)."""
+    meta: device uint8 tensor of 32 bytes (a dllm_meta).  events: optional pair of timing events
+    recorded right around the library call."""
     _need(row_req, torch.int32, "row_req", rows_cap)
     _need(meta, torch.uint8, "meta", 32)
     _need(status, torch.int32, "status", 1)
@@ -324,10 +338,9 @@ def dllm_compact(rows, L, W, mask_id, eos_id, row_req, rows_cap, reqs: ReqTable,
         _need(done, torch.uint8, "done", rows)
     st = reqs.struct()
     q = queue.struct()
-    rc = _lib.lib().dllm_compact(_stream(stream), rows, L, W, mask_id, eos_id, _ptr(box_ids), _ptr(mask), _ptr(done),
-                                 _ptr(row_req), rows_cap, ctypes.byref(st), ctypes.byref(q), int(budget), _ptr(meta),
-                                 _ptr(status))
-    _lib.check(rc, "dllm_compact")
+    args = (_stream(stream), rows, L, W, mask_id, eos_id, _ptr(box_ids), _ptr(mask), _ptr(done), _ptr(row_req),
+            rows_cap, ctypes.byref(st), ctypes.byref(q), int(budget), _ptr(meta), _ptr(status))
+    _launch(_lib.lib().dllm_compact, args, "dllm_compact", events, stream)
 
 
 def read_meta(meta_tensor) -> dict:

@@ -22,6 +22,17 @@ import torch
 from . import api
 
 
+def _around(events, fn):
+    """fn() between the two timing events (if any) on the current stream; the caller's forward is
+    timed this way, its own host work included."""
+    if events is None:
+        return fn()
+    events[0].record()
+    out = fn()
+    events[1].record()
+    return out
+
+
 class Session:
     """Device state for one run: request table, queue, row map, box buffers and step workspace."""
 
@@ -103,14 +114,13 @@ class Session:
             raise api.DllmError(s, where, "(device status)")
 
     def _timed(self, phase, timed, fn):
-        """fn(), bracketed by two events on the current stream when timed (the events cover the
-        device work fn enqueues, not host work after it)."""
+        """fn(events): when timed, `events` is a pair of timing events that fn records on the current
+        stream right around the work it enqueues (the library calls record them after marshalling
+        their arguments, so the interval holds no host work); otherwise None."""
         if not timed:
-            return fn()
+            return fn(None)
         ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        ev[0].record()
-        out = fn()
-        ev[1].record()
+        out = fn(ev)
         self.events[phase].append(ev)
         return out
 
@@ -124,9 +134,9 @@ class Session:
         kw = {}
         if with_box and self.rows > 0:
             kw = dict(box_ids=self.box_ids, mask=self.masks[self.cur], done=self.done)
-        self._timed("compact", timed, lambda: api.dllm_compact(
+        self._timed("compact", timed, lambda ev: api.dllm_compact(
             self.rows, self.L, self.W, self.mask_id, self.eos_id, self.row_req, self.rows_cap, self.reqs,
-            self.queue, self.budget, self.meta, self.status, **kw))
+            self.queue, self.budget, self.meta, self.status, events=ev, **kw))
         m = api.read_meta(self.meta)
         self.check_status("dllm_compact")
         self.rows, self.W = m["rows"], m["W"]
@@ -137,17 +147,18 @@ class Session:
         return m
 
     def pack(self, timed=False):
-        self._timed("pack", timed, lambda: api.dllm_pack(
+        self._timed("pack", timed, lambda ev: api.dllm_pack(
             self.rows, self.L, self.W, self.pad_id, self.row_req, self.reqs, self.box_ids, self.masks[self.cur],
-            self.tau, self.p_rows, self.b_rows, self.status, box_valid=self.box_valid, box_pos=self.box_pos))
+            self.tau, self.p_rows, self.b_rows, self.status, box_valid=self.box_valid, box_pos=self.box_pos,
+            events=ev))
         self.stats["packs"] += 1
 
     def step(self, timed=False):
         nxt = 1 - self.cur
-        self._timed("step", timed, lambda: api.dllm_step(
+        self._timed("step", timed, lambda ev: api.dllm_step(
             self.logits, self.box(), self.masks[self.cur], self.masks[nxt], self.tau, self.done, self.accept,
             self.workspace, self.status, p=self.p_rows, b=self.b_rows, conf=self.conf, argmax=self.argmax,
-            rows=self.rows, L=self.L, V=self.V, pos_stride=self.V, row_stride=self.L * self.V))
+            rows=self.rows, L=self.L, V=self.V, pos_stride=self.V, row_stride=self.L * self.V, events=ev))
         self.cur = nxt
 
     def features(self):
@@ -189,7 +200,7 @@ class Session:
                 self.stats["request_steps"] += self.rows
                 self.stats["idle_request_steps"] += int((~masked_rows).sum())
                 self.stats["positions_scored"] += int(masked.sum())
-                self._timed("forward", timed, lambda: forward(self))
+                self._timed("forward", timed, lambda ev: _around(ev, lambda: forward(self)))
                 self.step(timed=timed)
                 done, mask_host, st = self._readback()
                 if st != 0:
