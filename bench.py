@@ -337,6 +337,12 @@ def run_gpu(args):
     kev = {k: api.KernelEvents() for k in samples} if args.shards <= 1 else {}
     ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for k in samples} if args.shards > 1 else {}
+    # half a stride later, the whole dllm_step (threshold rule) is timed the same way: from the
+    # scoring kernel's start to the deciding kernel's end (dllm_step_timed)
+    half = args.ev_every // 2
+    sev = {k + half: api.KernelEvents() for k in samples
+           if half > 0 and k + half < n_total and k + half not in kev} \
+        if args.shards <= 1 and args.rule == "threshold" else {}
 
     def one(k):
         rc = lib.dllm_pack(*pack_args[k])
@@ -352,9 +358,13 @@ def run_gpu(args):
                 rc |= lib.dllm_step_score_shard(*sa[t])
         elif k in kev:
             rc |= lib.dllm_step_score_timed(*score_args[k % args.rotate], kev[k].start, kev[k].stop)
+        elif k in sev:
+            sa = score_args[k % args.rotate]
+            rc |= lib.dllm_step_timed(*sa[:8], *decide_args[5:], sev[k].start, sev[k].stop)
         else:
             rc |= lib.dllm_step_score(*score_args[k % args.rotate])
-        rc |= decide_fn(*decide_args)
+        if k not in sev:
+            rc |= decide_fn(*decide_args)
         if args.features:
             rc |= lib.dllm_step_features(*feat_args[k])
         rc |= lib.dllm_compact(*comp_args[k])
@@ -380,24 +390,36 @@ def run_gpu(args):
     cold_us = None
     if args.cold > 0 and args.shards <= 1:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        kernel_bound = args.rule == "threshold"
         cold_ev = []
         for k in range(args.cold + 2):
             flush.fill_(k & 0xFF)
-            e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            e[0].record()
-            rc |= lib.dllm_step_score(*score_args[k % args.rotate])
-            rc |= decide_fn(*decide_args)
-            e[1].record()
+            if kernel_bound:
+                # dllm_step with its events bound to the scoring kernel's start and the deciding
+                # kernel's end (the arguments of the two halves, in dllm_step's order)
+                e = api.KernelEvents()
+                sa, da = score_args[k % args.rotate], decide_args
+                rc |= lib.dllm_step_timed(*sa[:8], *da[5:], e.start, e.stop)
+            else:
+                e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                e[0].record()
+                rc |= lib.dllm_step_score(*score_args[k % args.rotate])
+                rc |= decide_fn(*decide_args)
+                e[1].record()
             if k >= 2:
                 cold_ev.append(e)
         torch.cuda.synchronize()
         if rc != 0:
             raise SystemExit(f"library error rc={rc}: {_lib.last_error()}")
-        cms = np.array([a.elapsed_time(b) for a, b in cold_ev]) * 1e3
-        cold_us = {"launches": int(cms.size), "p10": float(np.percentile(cms, 10)),
-                   "median": float(np.median(cms)), "p90": float(np.percentile(cms, 90)),
-                   "what": "dllm_step_score + dllm_step_decide between two HIP events, each launch after a "
-                           "1 GiB write that evicts L2 and the Infinity Cache"}
+        cms = np.array([e.elapsed_ms() if kernel_bound else e[0].elapsed_time(e[1]) for e in cold_ev]) * 1e3
+        med = float(np.median(cms))
+        cold_us = {"launches": int(cms.size), "p10": float(np.percentile(cms, 10)), "median": med,
+                   "p90": float(np.percentile(cms, 90)),
+                   "frac_of_peak_at_median": M * V * 2 / (med * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                   "what": ("dllm_step from the scoring kernel's start to the deciding kernel's end (HIP events "
+                            "bound to the two kernels, dllm_step_timed)" if kernel_bound else
+                            "dllm_step_score + dllm_step_decide between two HIP events recorded around the calls") +
+                           ", each launch after a 1 GiB write that evicts L2 and the Infinity Cache"}
         del flush
     timed_k = [k for k in samples if k >= args.warmup]
     if kev:
@@ -408,6 +430,7 @@ def run_gpu(args):
     for k, t in zip(timed_k, kern_ms):
         by_buf.setdefault(k % args.rotate, []).append(float(t) * 1e3)
     kern_s = float(kern_ms.mean()) / 1e3
+    step_ms = np.array([sev[k].elapsed_ms() for k in sorted(sev) if k >= args.warmup])
     step_bytes = M * V * 2
     timed_bytes = step_bytes if args.shards <= 1 else M * (V // args.shards) * 2
     achieved = timed_bytes / kern_s / 1e9
@@ -439,6 +462,12 @@ def run_gpu(args):
                                                  for b in range(args.rotate)],
                             "what": ("HIP events bound to the kernel's start and end (dllm_step_score_timed)"
                                      if kev else "HIP events recorded around the call")},
+        **({"dllm_step_us": {"samples": int(step_ms.size), "mean": float(step_ms.mean()) * 1e3,
+                             "p50": float(np.percentile(step_ms, 50)) * 1e3,
+                             "frac_of_peak_at_mean": step_bytes / (float(step_ms.mean()) * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                             "what": "dllm_step (score + decide) inside the timed loop, from the scoring kernel's "
+                                     "start to the deciding kernel's end (dllm_step_timed), half a stride after "
+                                     "each scoring-kernel timing"}} if step_ms.size else {}),
         **({"dllm_step_cold_us": cold_us} if cold_us else {}),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,

@@ -120,6 +120,21 @@ def dllm_step(logits, input_ids, mask_in, mask_out, threshold, done, accept_len,
     _launch(_lib.lib().dllm_step, args, "dllm_step", events, stream)
 
 
+def dllm_step_timed(logits, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status, kernel_events,
+                    p=None, b=None, conf=None, argmax=None, rows=None, L=None, V=None, pos_stride=None,
+                    row_stride=None, stream=None):
+    """dllm_step with `kernel_events` (a KernelEvents) bound to the scoring kernel's start and the
+    deciding kernel's end."""
+    rows, L, V, pos_stride, row_stride = _logits_shape(logits, rows, L, V, pos_stride, row_stride)
+    W = _decide_args(rows, L, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status, p, b,
+                     conf, argmax)
+    args = (_stream(stream), _ptr(logits), _DT[logits.dtype], pos_stride, row_stride, rows, L, V, _ptr(input_ids), W,
+            _ptr(mask_in), _ptr(mask_out), _ptr(threshold), _ptr(p), _ptr(b), _ptr(conf), _ptr(argmax), _ptr(done),
+            _ptr(accept_len), _ptr(workspace), workspace.numel(), _ptr(status), kernel_events.start,
+            kernel_events.stop)
+    _launch(_lib.lib().dllm_step_timed, args, "dllm_step_timed", None, stream)
+
+
 def dllm_step_score(logits, mask_in, workspace, status, rows=None, L=None, V=None, pos_stride=None,
                     row_stride=None, stream=None):
     """The scoring half of dllm_step: per-chunk partials of every masked slot into `workspace`."""

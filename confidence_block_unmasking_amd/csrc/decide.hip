@@ -210,18 +210,27 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
 
 
 template <int G>
-void launch_decide_g(const StepParams &P, hipStream_t st, int mode) {
+void launch_decide_g(const StepParams &P, hipStream_t st, int mode, hipEvent_t ev_stop) {
     const size_t lds = (size_t)P.L * 10 + 16;
     const dim3 grid((unsigned)P.rows), block(kDecideThreads);
-    if (mode == kRuleQuota) hipLaunchKernelGGL((decide_kernel<kRuleQuota, G>), grid, block, lds, st, P);
-    else if (mode == kEmitTriples) hipLaunchKernelGGL((decide_kernel<kEmitTriples, G>), grid, block, lds, st, P);
-    else hipLaunchKernelGGL((decide_kernel<kRuleThreshold, G>), grid, block, lds, st, P);
+    // with ev_stop: the same launch, the event taking the kernel's own end time
+    auto go = [&](auto kernel) {
+        if (ev_stop) hipExtLaunchKernelGGL(kernel, grid, block, lds, st, nullptr, ev_stop, 0, P);
+        else hipLaunchKernelGGL(kernel, grid, block, lds, st, P);
+    };
+    if (mode == kRuleQuota) go(decide_kernel<kRuleQuota, G>);
+    else if (mode == kEmitTriples) go(decide_kernel<kEmitTriples, G>);
+    else go(decide_kernel<kRuleThreshold, G>);
+}
+
+dllm_status launch_decide_ev(const StepParams &P, hipStream_t st, int mode, hipEvent_t ev_stop) {
+    if (P.L <= kDecideWaves * 4) launch_decide_g<4>(P, st, mode, ev_stop);
+    else launch_decide_g<8>(P, st, mode, ev_stop);
+    return check_hip(hipGetLastError(), "dllm_step decide launch");
 }
 
 dllm_status launch_decide(const StepParams &P, hipStream_t st, int mode) {
-    if (P.L <= kDecideWaves * 4) launch_decide_g<4>(P, st, mode);
-    else launch_decide_g<8>(P, st, mode);
-    return check_hip(hipGetLastError(), "dllm_step decide launch");
+    return launch_decide_ev(P, st, mode, nullptr);
 }
 
 

@@ -37,6 +37,11 @@
 // decide.hip, their shared definitions in step_common.h.
 #include "step_common.h"
 
+namespace dllm {
+// decide.hip: launch_decide with an event bound to the deciding kernel's end (nullptr: none)
+dllm_status launch_decide_ev(const StepParams &P, hipStream_t st, int mode, hipEvent_t ev_stop);
+}  // namespace dllm
+
 namespace {
 
 using namespace dllm;
@@ -143,6 +148,26 @@ extern "C" dllm_status dllm_step(void *stream, const void *logits, int32_t dtype
     rc = launch_score(P, dtype, (hipStream_t)stream);
     if (rc != DLLM_OK) return rc;
     return launch_decide(P, (hipStream_t)stream, P.S > 0 ? kRuleQuota : kRuleThreshold);
+}
+
+extern "C" dllm_status dllm_step_timed(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
+                                       int64_t row_stride, int32_t rows, int32_t L, int32_t V, int32_t *input_ids,
+                                       int32_t W, const uint8_t *mask_in, uint8_t *mask_out, const float *threshold,
+                                       const int32_t *p, const int32_t *b, float *conf, int32_t *argmax,
+                                       uint8_t *done, int32_t *accept_len, void *workspace, size_t workspace_bytes,
+                                       int32_t *status, void *start_event, void *stop_event) {
+    if (!start_event || !stop_event) return fail(DLLM_ERR_ARG, "dllm_step_timed: null event");
+    StepParams P{};
+    dllm_status rc = check_shape("dllm_step_timed", dtype, rows, L, V, workspace, P);
+    if (rc == DLLM_OK) rc = check_score("dllm_step_timed", logits, dtype, pos_stride, row_stride, mask_in, status, P);
+    if (rc == DLLM_OK)
+        rc = check_decide("dllm_step_timed", input_ids, W, mask_in, mask_out, threshold, 0, p, b, conf, argmax, done,
+                          accept_len, status, P);
+    if (rc == DLLM_OK) rc = check_workspace("dllm_step_timed", dtype, workspace, workspace_bytes, P);
+    if (rc != DLLM_OK || rows == 0) return rc;
+    rc = launch_score(P, dtype, (hipStream_t)stream, (hipEvent_t)start_event, nullptr);
+    if (rc != DLLM_OK) return rc;
+    return launch_decide_ev(P, (hipStream_t)stream, kRuleThreshold, (hipEvent_t)stop_event);
 }
 
 extern "C" dllm_status dllm_step_score(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,

@@ -135,6 +135,19 @@ dllm_status dllm_step(void *stream, const void *logits, int32_t dtype, int64_t p
                       const int32_t *p, const int32_t *b, float *conf, int32_t *argmax, uint8_t *done,
                       int32_t *accept_len, void *workspace, size_t workspace_bytes, int32_t *status);
 
+/* dllm_step_timed — dllm_step with its device time measured: start_event takes the start of the
+ * scoring kernel and stop_event the end of the deciding kernel (hipEvent_t handles created with
+ * timing enabled, owned by the caller), so hipEventElapsedTime gives the step from the first
+ * kernel's start to the second's end, without the dispatch latency an event pair recorded around
+ * the call also holds.  Outputs, status and errors as for dllm_step, plus DLLM_ERR_ARG for a null
+ * event.  With rows == 0 nothing is launched and the events are not recorded. */
+dllm_status dllm_step_timed(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
+                            int64_t row_stride, int32_t rows, int32_t L, int32_t V, int32_t *input_ids,
+                            int32_t W, const uint8_t *mask_in, uint8_t *mask_out, const float *threshold,
+                            const int32_t *p, const int32_t *b, float *conf, int32_t *argmax, uint8_t *done,
+                            int32_t *accept_len, void *workspace, size_t workspace_bytes, int32_t *status,
+                            void *start_event, void *stop_event);
+
 /* Bytes of workspace dllm_step (or the pair below) needs for this shape (0 for invalid
  * arguments). */
 size_t dllm_step_workspace_bytes(int32_t rows, int32_t L, int32_t V, int32_t dtype);

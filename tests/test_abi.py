@@ -132,6 +132,27 @@ def test_timed_score_rejects_bad_arguments():
     assert timed(rows=0, logits=None, mask=None) == _lib.DLLM_OK
 
 
+def test_timed_step_rejects_bad_arguments():
+    L = _lib.lib()
+    need = L.dllm_step_workspace_bytes(4, 32, 1024, 1)
+    f, ws, ev = FAKE, ctypes.c_void_p(0x10000), ctypes.c_void_p(0x3000)
+
+    def timed(**kw):
+        a = dict(logits=f, dtype=1, rows=4, W=40, ws=ws, n=need, e0=ev, e1=ev, done=f)
+        a.update(kw)
+        return L.dllm_step_timed(None, a["logits"], a["dtype"], 1024, 32 * 1024, a["rows"], 32, 1024, f, a["W"], f,
+                                 ctypes.c_void_p(0x2000), f, None, None, None, None, a["done"], f, a["ws"], a["n"], f,
+                                 a["e0"], a["e1"])
+    assert timed(e0=None) == _lib.DLLM_ERR_ARG
+    assert timed(e1=None) == _lib.DLLM_ERR_ARG
+    assert "event" in _lib.last_error()
+    assert timed(dtype=7) == _lib.DLLM_ERR_DTYPE
+    assert timed(W=31) == _lib.DLLM_ERR_SHAPE
+    assert timed(done=None) == _lib.DLLM_ERR_ARG
+    assert timed(n=need - 16) == _lib.DLLM_ERR_ARG
+    assert timed(rows=0, logits=None) == _lib.DLLM_OK
+
+
 def test_quota_rejects_bad_arguments():
     L = _lib.lib()
     need = L.dllm_step_workspace_bytes(4, 32, 1024, 1)

@@ -295,6 +295,20 @@ def test_step_halves_equal_step():
              conf=conf.cpu().numpy(), argmax=arg.cpu().numpy())
     for k in c:
         assert np.array_equal(a[k], c[k]), k
+    # the whole step timed from the scoring kernel's start to the deciding kernel's end: same outputs,
+    # and an interval that holds the scoring kernel's
+    ids.copy_(torch.from_numpy(pk["box_ids"].astype(np.int32)))
+    ws.fill_(0x5A)
+    ev2 = api.KernelEvents()
+    api.dllm_step_timed(lg, ids, mask, mout, tau, done, acc, ws, status, ev2, conf=conf, argmax=arg)
+    ms2 = ev2.elapsed_ms()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert 0.5 * ms < ms2 < 1000.0
+    d = dict(ids=ids.cpu().numpy(), mask=mout.cpu().numpy(), done=done.cpu().numpy(), accept=acc.cpu().numpy(),
+             conf=conf.cpu().numpy(), argmax=arg.cpu().numpy())
+    for k in d:
+        assert np.array_equal(a[k], d[k]), k
 
 
 def test_step_in_place_mask_update():
