@@ -66,6 +66,9 @@ def _logits_shape(logits, rows, L, V, pos_stride, row_stride):
     r*row_stride + j*pos_stride + v, so the tensor's storage must reach that far."""
     if logits.dtype not in _DT:
         raise ValueError(f"logits dtype {logits.dtype} not supported")
+    # the kernels read a slot's V elements as one contiguous run
+    if logits.dim() >= 1 and logits.shape[-1] > 1 and logits.stride(-1) != 1:
+        raise ValueError(f"logits must have unit stride along the vocabulary, got stride {logits.stride(-1)}")
     if not logits.is_cuda:
         raise ValueError("logits must be a device tensor")
     if rows is None:

@@ -278,3 +278,17 @@ def test_binding_limits_match_the_header():
     got = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define DLLM_(MAX_\w+)\s+(\d+)", text)}
     assert got["MAX_L"] == _lib.MAX_L and got["MAX_ROWS"] == _lib.MAX_ROWS
     assert got["MAX_POSITIONS"] == _lib.MAX_POSITIONS and got["MAX_QUEUE"] == _lib.MAX_QUEUE
+
+
+def test_binding_rejects_a_strided_vocabulary():
+    """The kernels read each slot's vocabulary row as one contiguous run: a view whose last
+    dimension is strided (x[..., ::2]) is refused before anything reaches the library."""
+    torch = pytest.importorskip("torch")
+    from confidence_block_unmasking_amd import api
+    x = torch.zeros(2, 3, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="unit stride"):
+        api._logits_shape(x[..., ::2], None, None, None, None, None)
+    with pytest.raises(ValueError, match="unit stride"):
+        api._logits_shape(x.reshape(-1)[::2], 2, 3, 16, 16, 48)
+    with pytest.raises(ValueError, match="device tensor"):          # a contiguous view passes the stride test
+        api._logits_shape(x[..., :8], None, None, None, None, None)

@@ -40,3 +40,24 @@ def test_feature_invariants():
                 assert f[6] == np.sort(c)[n // 2]
         else:
             assert np.isnan(f[4:]).all()
+
+
+def test_features_of_a_box_row_by_row():
+    """features() over a box: each row takes its own threshold, block index and block count.  The
+    rows are the hand-worked L = 4 examples, in an order unlike the file's, so a row that read
+    another row's threshold, b or K (or its confidences or mask) would show."""
+    four = [e for e in EX["examples"] if e["L"] == 4]
+    assert len(four) == 4 and len({(e["tau"], e["b"], e["K"]) for e in four}) == 4
+    order = [3, 0, 2, 1]
+    rows = [four[i] for i in order]
+    conf = np.array([e["conf"] for e in rows], np.float64)
+    after = np.array([e["mask_after"] for e in rows], np.uint8)
+    tau = np.array([e["tau"] for e in rows], np.float32)
+    b = np.array([e["b"] for e in rows], np.int64)
+    K = np.array([e["K"] for e in rows], np.int64)
+    f = ofeat.features(conf, after, tau, b, K, 4)
+    assert f.shape == (4, len(ofeat.NAMES))
+    for r, e in enumerate(rows):
+        want = np.array([np.nan if v is None else v for v in e["features"]])
+        assert np.allclose(f[r], want, rtol=0, atol=1e-12, equal_nan=True), (r, f[r], want)
+    assert ofeat.features(np.zeros((0, 4)), np.zeros((0, 4), np.uint8), tau[:0], b[:0], K[:0], 4).shape == (0, 9)

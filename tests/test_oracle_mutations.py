@@ -74,6 +74,11 @@ MUTATIONS = [
      LOOP),
     ("oracle/shard.py", "    return m, offset + a, S", "    return m, a, S", SHARD),
     ("oracle/quota.py", "    for j in js[:max(0, int(k))]:", "    for j in js[:max(0, int(k) - 1)]:", QUOTA),
+    # a row-index slip in the per-box wrapper of the features
+    ("oracle/features.py", "threshold[r], int(b[r]), int(K[r]), L)", "threshold[0], int(b[r]), int(K[r]), L)", FEAT),
+    ("oracle/features.py", "threshold[r], int(b[r]), int(K[r]), L)", "threshold[r], int(b[0]), int(K[r]), L)", FEAT),
+    ("oracle/features.py", "threshold[r], int(b[r]), int(K[r]), L)", "threshold[r], int(b[r]), int(K[-1]), L)", FEAT),
+    ("oracle/features.py", "row_features(conf[r], mask_after[r],", "row_features(conf[r], mask_after[0],", FEAT),
 ]
 
 
