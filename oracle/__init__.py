@@ -11,6 +11,9 @@ by eye, with no blocking, fusion or reordering:
   pack.py     left-padded bounding-box materialisation with position ids
   compact.py  block-boundary scatter, advance/evict, token-budget admission, row layout
   loop.py     synchronous and first-done-first-out loops, idle request-step accounting
+  rows.py     the per-slot confidence/argmax of step.py in C (rows.c), for replaying whole loops
+  quota.py, shard.py, features.py   the next rows: fixed per-step quota, vocabulary shards,
+              step-predictor features
 
 Citation key (page titles):
   [FDFO]       "FDFO: 让 dLLM 推理从「整批等最慢」变成「谁先完成谁先走」"

@@ -2,10 +2,15 @@
 
 Each loop runs the GPU path (synthetic logits from the GPU generator, then dllm_step, dllm_pack and
 dllm_compact through the C ABI) and, beside it, the oracle's pack and compact on a host copy of the
-state fed with the same step outcomes.  Every pack and compact result is compared exactly; every
-step is checked against the unmask rule on the GPU's own confidences (all rows) and against the
-oracle's scores (all slots when few, else a seeded sample plus whole rows), with the oracle's logits
-rows produced by the CPU generator, not read back from the GPU.
+state fed with the same step outcomes.  Every pack and compact result is compared exactly, and every
+step's decision is checked against the unmask rule on the GPU's own confidences (all rows).
+Scores and decisions against the oracle's own confidences:
+  * small runs: every scored slot, by step.py on rows from the CPU generator;
+  * the LLaDA-shaped and BlockServe runs: every scored slot of every step, by the oracle's C scorer
+    (tests/loopcheck.py) on the rows the step read, plus a few slots per step on CPU-generated rows;
+  * the large FDFO run: every slot the GPU unmasks in every step and every scored slot of every
+    other step (two tests, even and odd steps), the same way.
+No token the GPU chooses enters the oracle's state unchecked.
 """
 import numpy as np
 import pytest
@@ -15,6 +20,7 @@ from oracle import features as ofeat
 from oracle import loop as oloop
 from oracle import pack as opack
 from oracle import step as ostep
+from tests.loopcheck import DeferredChecker
 from tests.parity import CONF_TOL, ambiguous_row
 from workload import configs, synth
 
@@ -68,107 +74,157 @@ def _check_features(sess, st, rows, L, g_conf, g_mask):
 
 
 def lockstep_run(w, full_score_max=64, sample=16, whole_rows=1, deep_every=1, seed=0, label="", eos_id=-1,
-                 features_every=1):
+                 features_every=1, deferred=False, check_all=None):
+    """Run workload w on the GPU in lockstep with the oracle's pack and compact.
+
+    Synchronous mode (deferred=False): a step with at most full_score_max masked slots is scored in
+    full by the oracle (step.py) on rows from the CPU generator; a larger one on `sample` random
+    slots plus `whole_rows` whole rows.
+    Deferred mode: every slot the GPU unmasks in a step, and on steps where check_all(step, meta)
+    holds every slot it scores, is checked by a DeferredChecker (the oracle's C scorer on the rows
+    the step read); `sample` random slots per step are still checked synchronously on CPU-generated
+    rows.  No GPU token is adopted that the oracle does not confirm.
+    """
     from confidence_block_unmasking_amd.driver import Session
     rng = np.random.default_rng(seed)
     sess = Session.from_workload(w, eos_id=eos_id)
     st = _oracle_state(w)
     L, V = w.L, w.V
     fwd = gpu_forward(w)
+    checker = DeferredChecker(w.dtype, V) if deferred else None
     mg = sess.compact(with_box=False)
     mo = ocompact.compact(st, w.rows, L, 0, w.mask_id, eos_id, w.budget, w.rows_cap)
     _compare_meta(mg, mo)
     _compare_tables(sess, st)
     n_steps = n_scored = n_checked = n_amb = n_compacts = 0
+    n_unmasked = n_unmasked_checked = n_dev = n_full_steps = 0
     max_err = 0.0
-    while sess.rows > 0:
-        rows, W = sess.rows, sess.W
-        sess.pack()
-        pk = opack.pack(st["row_req"], rows, L, W, w.pad_id, st["p"], st["b"], st["threshold"], st["arena_off"],
-                        st["arena"], st["blk_mask"])
-        assert np.array_equal(sess.box().cpu().numpy(), pk["box_ids"]), "box_ids"
-        assert np.array_equal(sess.box_valid[:rows * W].view(rows, W).cpu().numpy(), pk["box_valid"]), "box_valid"
-        assert np.array_equal(sess.box_pos[:rows * W].view(rows, W).cpu().numpy(), pk["box_pos"]), "box_pos"
-        assert np.array_equal(sess.mask().cpu().numpy(), pk["mask"]), "mask"
-        assert np.array_equal(sess.tau[:rows].cpu().numpy(), pk["threshold"]), "threshold"
-        assert np.array_equal(sess.p_rows[:rows].cpu().numpy(), pk["p"]) and \
-            np.array_equal(sess.b_rows[:rows].cpu().numpy(), pk["b"]), "p/b"
-        ids_o, mask_o = pk["box_ids"].copy(), pk["mask"].copy()
-        while True:
-            fwd(sess)
-            sess.step()
-            n_steps += 1
-            g_ids = sess.box().cpu().numpy()
-            g_mask = sess.mask().cpu().numpy()
-            g_done = sess.done[:rows].cpu().numpy()
-            g_acc = sess.accept[:rows].cpu().numpy()
-            g_conf = sess.conf[:rows * L].view(rows, L).cpu().numpy()
-            g_arg = sess.argmax[:rows * L].view(rows, L).cpu().numpy()
-            assert int(sess.status.item()) == 0
-            masked = mask_o != 0
-            M = int(masked.sum())
-            n_scored += M
-            # scores against the oracle on CPU-generated rows
-            slots = list(zip(*np.nonzero(masked)))
-            if M > full_score_max:
-                pick = rng.choice(M, size=min(sample, M), replace=False)
-                chosen = {slots[i] for i in pick}
-                rows_full = rng.choice(np.flatnonzero(masked.any(1)), size=min(whole_rows, int(masked.any(1).sum())),
-                                       replace=False)
-                for r in rows_full:
-                    chosen |= {(r, j) for j in np.flatnonzero(masked[r])}
-            else:
-                chosen = set(slots)
-            o_conf = np.full((rows, L), np.nan)
-            for (r, j) in sorted(chosen):
-                x = synth.row_cpu(V, w.dtype, w.logit_seed, int(st["row_req"][r]), int(pk["b"][r]), int(j),
-                                  int(masked[r].sum()), w.sigma, w.umax)
-                _, a, _, c = ostep.score(ostep.widen(x, w.dtype))
-                assert g_arg[r, j] == a, f"argmax at row {r} slot {j}"
-                err = abs(float(g_conf[r, j]) - c)
-                assert err <= CONF_TOL, f"conf at row {r} slot {j}: {err}"
-                max_err = max(max_err, err)
-                o_conf[r, j] = c
-                n_checked += 1
-            # decisions: (iii) on every row, (iv) on rows whose masked slots were all scored
-            for r in range(rows):
-                U = masked[r] & (g_mask[r] == 0)
-                assert np.array_equal(U, ostep.decide(g_conf[r].astype(np.float64), masked[r], pk["threshold"][r]))
-                if masked[r].any() and not np.isnan(o_conf[r][masked[r]]).any():
-                    if ambiguous_row(o_conf[r], masked[r], pk["threshold"][r]):
-                        n_amb += 1
-                    else:
-                        assert np.array_equal(U, ostep.decide(o_conf[r], masked[r], pk["threshold"][r])), r
-                assert np.all(g_arg[r][~masked[r]] == -1)
-                # write-back of the adopted decision, exactly
-                for j in np.flatnonzero(U):
+    try:
+        while sess.rows > 0:
+            rows, W = sess.rows, sess.W
+            sess.pack()
+            pk = opack.pack(st["row_req"], rows, L, W, w.pad_id, st["p"], st["b"], st["threshold"], st["arena_off"],
+                            st["arena"], st["blk_mask"])
+            assert np.array_equal(sess.box().cpu().numpy(), pk["box_ids"]), "box_ids"
+            assert np.array_equal(sess.box_valid[:rows * W].view(rows, W).cpu().numpy(), pk["box_valid"]), "box_valid"
+            assert np.array_equal(sess.box_pos[:rows * W].view(rows, W).cpu().numpy(), pk["box_pos"]), "box_pos"
+            assert np.array_equal(sess.mask().cpu().numpy(), pk["mask"]), "mask"
+            assert np.array_equal(sess.tau[:rows].cpu().numpy(), pk["threshold"]), "threshold"
+            assert np.array_equal(sess.p_rows[:rows].cpu().numpy(), pk["p"]) and \
+                np.array_equal(sess.b_rows[:rows].cpu().numpy(), pk["b"]), "p/b"
+            ids_o, mask_o = pk["box_ids"].copy(), pk["mask"].copy()
+            while True:
+                fwd(sess)
+                sess.step()
+                n_steps += 1
+                g_ids = sess.box().cpu().numpy()
+                g_mask = sess.mask().cpu().numpy()
+                g_done = sess.done[:rows].cpu().numpy()
+                g_acc = sess.accept[:rows].cpu().numpy()
+                g_conf = sess.conf[:rows * L].view(rows, L).cpu().numpy()
+                g_arg = sess.argmax[:rows * L].view(rows, L).cpu().numpy()
+                assert int(sess.status.item()) == 0
+                masked = mask_o != 0
+                M = int(masked.sum())
+                n_scored += M
+                U_all = masked & (g_mask == 0)
+                n_unmasked += int(U_all.sum())
+                # (iii) on every row: the GPU's decision is the rule on its own confidences
+                for r in range(rows):
+                    assert np.array_equal(U_all[r], ostep.decide(g_conf[r].astype(np.float64), masked[r],
+                                                                 pk["threshold"][r])), f"row {r}: rule (iii)"
+                    assert np.all(g_arg[r][~masked[r]] == -1)
+                if deferred:
+                    # every unmasked slot, or every scored slot on the chosen steps, by the C oracle
+                    full = check_all is not None and check_all(n_steps, mg)
+                    n_full_steps += int(full)
+                    sel = masked if full else U_all
+                    rr, jj = np.nonzero(sel)
+                    slots = list(zip(rr.tolist(), jj.tolist()))
+                    rows_full = [(r, masked[r].copy(), pk["threshold"][r], U_all[r].copy())
+                                 for r in np.flatnonzero(masked.any(1)) if np.array_equal(sel[r], masked[r])]
+                    host = checker.gather(sess.logits, rr * L + jj)
+                    checker.submit(n_steps, host, slots, g_arg[rr, jj], g_conf[rr, jj], rows_full)
+                    n_dev += len(slots)
+                    n_unmasked_checked += int((sel & U_all).sum())
+                    chosen = set()
+                    if sample and M:
+                        sl = list(zip(*np.nonzero(masked)))
+                        chosen = {sl[i] for i in rng.choice(M, size=min(sample, M), replace=False)}
+                elif M > full_score_max:
+                    slots = list(zip(*np.nonzero(masked)))
+                    pick = rng.choice(M, size=min(sample, M), replace=False)
+                    chosen = {slots[i] for i in pick}
+                    rows_full = rng.choice(np.flatnonzero(masked.any(1)),
+                                           size=min(whole_rows, int(masked.any(1).sum())), replace=False)
+                    for r in rows_full:
+                        chosen |= {(r, j) for j in np.flatnonzero(masked[r])}
+                else:
+                    chosen = set(zip(*np.nonzero(masked)))
+                # scores against the oracle (step.py) on CPU-generated rows
+                o_conf = np.full((rows, L), np.nan)
+                for (r, j) in sorted(chosen):
+                    x = synth.row_cpu(V, w.dtype, w.logit_seed, int(st["row_req"][r]), int(pk["b"][r]), int(j),
+                                      int(masked[r].sum()), w.sigma, w.umax)
+                    _, a, _, c = ostep.score(ostep.widen(x, w.dtype))
+                    assert g_arg[r, j] == a, f"argmax at row {r} slot {j}"
+                    err = abs(float(g_conf[r, j]) - c)
+                    assert err <= CONF_TOL, f"conf at row {r} slot {j}: {err}"
+                    max_err = max(max_err, err)
+                    o_conf[r, j] = c
+                    n_checked += 1
+                    n_unmasked_checked += int(not deferred and U_all[r, j])
+                # (iv) on rows whose masked slots were all scored here
+                for r in range(rows):
+                    if masked[r].any() and not np.isnan(o_conf[r][masked[r]]).any():
+                        if ambiguous_row(o_conf[r], masked[r], pk["threshold"][r]):
+                            n_amb += 1
+                        else:
+                            assert np.array_equal(U_all[r], ostep.decide(o_conf[r], masked[r], pk["threshold"][r])), r
+                # write-back of the decision (every adopted token is one the oracle checks)
+                for r, j in zip(*np.nonzero(U_all)):
                     ids_o[r, W - L + j] = g_arg[r, j]
-            mask_o = (masked & ~(g_mask == 0)).astype(np.uint8)
-            done_o = (~(mask_o != 0).any(1)).astype(np.uint8)
-            assert np.array_equal(g_ids, ids_o), "ids"
-            assert np.array_equal(g_mask, mask_o), "mask"
-            assert np.array_equal(g_done, done_o), "done"
-            assert np.array_equal(g_acc, np.where(done_o == 1, L, 0)), "accept"
-            if n_steps % features_every == 0:
-                _check_features(sess, st, rows, L, g_conf, g_mask)
-            if w.mode == "fdfo" and done_o.any():
-                break
-            if w.mode == "sync" and done_o.all():
-                break
-        mg = sess.compact(with_box=True)
-        mo = ocompact.compact(st, rows, L, W, w.mask_id, eos_id, w.budget, w.rows_cap, box_ids=ids_o, mask=mask_o,
-                              done=done_o)
-        n_compacts += 1
-        _compare_meta(mg, mo)
-        _compare_tables(sess, st, deep=(n_compacts % deep_every == 0))
-        if n_compacts % 50 == 0:
-            print(f"{label} compacts={n_compacts} steps={n_steps} rows={mg['rows']} W={mg['W']} "
-                  f"queued={mg['n_queued']}", flush=True)
+                mask_o = (masked & ~U_all).astype(np.uint8)
+                done_o = (~(mask_o != 0).any(1)).astype(np.uint8)
+                assert np.array_equal(g_ids, ids_o), "ids"
+                assert np.array_equal(g_mask, mask_o), "mask"
+                assert np.array_equal(g_done, done_o), "done"
+                assert np.array_equal(g_acc, np.where(done_o == 1, L, 0)), "accept"
+                if n_steps % features_every == 0:
+                    _check_features(sess, st, rows, L, g_conf, g_mask)
+                if w.mode == "fdfo" and done_o.any():
+                    break
+                if w.mode == "sync" and done_o.all():
+                    break
+            mg = sess.compact(with_box=True)
+            mo = ocompact.compact(st, rows, L, W, w.mask_id, eos_id, w.budget, w.rows_cap, box_ids=ids_o,
+                                  mask=mask_o, done=done_o)
+            n_compacts += 1
+            _compare_meta(mg, mo)
+            _compare_tables(sess, st, deep=(n_compacts % deep_every == 0))
+            if n_compacts % 50 == 0:
+                print(f"{label} compacts={n_compacts} steps={n_steps} rows={mg['rows']} W={mg['W']} "
+                      f"queued={mg['n_queued']}", flush=True)
+    finally:
+        if checker is not None:
+            cst = checker.finish()
     _compare_tables(sess, st, deep=True)
     assert np.all(st["state"] == configs.FINISHED)
-    print(f"{label}: steps={n_steps} scored={n_scored} checked={n_checked} ambiguous_rows={n_amb} "
-          f"max_conf_err={max_err:.3g}", flush=True)
+    if deferred:
+        n_amb += cst["ambiguous"]
+        max_err = max(max_err, cst["max_err"])
+        assert cst["slots"] == n_dev, (cst, n_dev)
+        assert n_unmasked_checked == n_unmasked, (n_unmasked_checked, n_unmasked)
+    print(f"{label}: steps={n_steps} scored={n_scored} checked_sync={n_checked} "
+          f"checked_deferred={n_dev} ({(n_dev + n_checked) / max(n_scored, 1):.1%} of scored; "
+          f"every-slot steps {n_full_steps}) unmasked={n_unmasked} unmasked_checked={n_unmasked_checked} "
+          f"ambiguous_rows={n_amb} max_conf_err={max_err:.3g}", flush=True)
+    if deferred:
+        print(f"{label}: oracle C scorer {cst['score_s']:.1f} s wall on {checker.threads} threads for "
+              f"{cst['slots']} rows ({cst['slots'] / max(cst['score_s'], 1e-9):.0f} rows/s, "
+              f"{cst['elems'] / max(cst['score_s'], 1e-9) / 1e9:.2f} G logits/s)", flush=True)
     return dict(steps=n_steps, scored=n_scored, amb=n_amb, arena=st["arena"].copy(), stats=sess.stats,
+                checked=n_checked + n_dev, unmasked=n_unmasked, unmasked_checked=n_unmasked_checked,
                 early=int(((st["state"] == configs.FINISHED) & (st["b"] < st["K"])).sum()))
 
 
@@ -277,17 +333,27 @@ def test_loop_tiny_step_sync():
 
 
 def test_loop_llada_sync():
-    lockstep_run(configs.llada_sync(), full_score_max=32, sample=32, whole_rows=1, label="llada")
+    """The LLaDA-shaped synchronous run: every scored slot of every step checked by the oracle."""
+    res = lockstep_run(configs.llada_sync(), sample=4, label="llada", deferred=True, check_all=lambda k, m: True)
+    assert res["checked"] >= res["scored"]
 
 
 def test_loop_blockserve_mixed_fdfo():
-    lockstep_run(configs.blockserve_mixed(), full_score_max=0, sample=4, whole_rows=0, deep_every=5, label="blockserve",
-                 features_every=10)
+    """The BlockServe mixed-state FDFO run: every scored slot of every step (about 2.4 million
+    vocabulary rows) checked by the oracle."""
+    res = lockstep_run(configs.blockserve_mixed(), sample=2, deep_every=5, label="blockserve", features_every=10,
+                       deferred=True, check_all=lambda k, m: True)
+    assert res["checked"] >= res["scored"]
 
 
-def test_loop_large_fdfo():
-    lockstep_run(configs.large_fdfo(), full_score_max=0, sample=2, whole_rows=0, deep_every=25, label="large",
-                 features_every=25)
+@pytest.mark.parametrize("half", [0, 1])
+def test_loop_large_fdfo(half):
+    """The large FDFO run (about 12.4 million scored slots): every slot the GPU unmasks in every
+    step, and every scored slot of every other step (the even steps in one half of the test, the
+    odd ones in the other), checked by the oracle.  Together the two halves check every slot."""
+    res = lockstep_run(configs.large_fdfo(), sample=2, deep_every=25, label=f"large[{half}]", features_every=25,
+                       deferred=True, check_all=lambda k, m: k % 2 == half)
+    assert res["checked"] >= 0.45 * res["scored"], res["checked"] / res["scored"]
 
 
 def _abc_session(T, L=8, V=16):

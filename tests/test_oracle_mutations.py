@@ -20,6 +20,7 @@ LOOP = "tests/test_oracle_loop.py"
 QUOTA = "tests/test_oracle_quota.py"
 FEAT = "tests/test_oracle_features.py"
 SHARD = "tests/test_oracle_shard.py"
+ROWS = "tests/test_oracle_rows.py"
 
 MUTATIONS = [
     ("oracle/step.py", "S = float(np.sum(np.exp(x - m)))", "S = float(np.sum(np.exp(m - x)))", STEP),
@@ -79,13 +80,22 @@ MUTATIONS = [
     ("oracle/features.py", "threshold[r], int(b[r]), int(K[r]), L)", "threshold[r], int(b[0]), int(K[r]), L)", FEAT),
     ("oracle/features.py", "threshold[r], int(b[r]), int(K[r]), L)", "threshold[r], int(b[r]), int(K[-1]), L)", FEAT),
     ("oracle/features.py", "row_features(conf[r], mask_after[r],", "row_features(conf[r], mask_after[0],", FEAT),
+    # the C row scorer (rebuilt from the planted source in the scratch copy)
+    ("oracle/rows.c", "S += exp(buf[v] - m);", "S += exp(m - buf[v]);", ROWS),
+    ("oracle/rows.c", "for (int64_t v = 0; v < V; ++v) S += exp", "for (int64_t v = 1; v < V; ++v) S += exp", ROWS),
+    ("oracle/rows.c", "    int64_t a = 0;\n", "    int64_t a = 1;\n", ROWS),
+    ("oracle/rows.c", "m = buf[v] > m ? buf[v] : m;", "m = buf[v] < m ? buf[v] : m;", ROWS),
+    ("oracle/rows.c", "*conf = 1.0 / S;", "*conf = 1.0 / (S + 1.0);", ROWS),
+    ("oracle/rows.c", "uint32_t u = (uint32_t)h[v] << 16;", "uint32_t u = (uint32_t)h[v] << 15;", ROWS),
+    ("oracle/rows.c", "finite &= fabs(buf[v]) <= DBL_MAX;", "finite &= fabs(buf[v]) <= INFINITY;", ROWS),
+    ("oracle/rows.c", "(size_t)i * (size_t)row_stride * es", "(size_t)i * (size_t)V * es", ROWS),
 ]
 
 
 def _copy_tree(dst):
     for d in ("oracle", "workload", "tests"):
         shutil.copytree(os.path.join(ROOT, d), os.path.join(dst, d),
-                        ignore=shutil.ignore_patterns("__pycache__", "golden_tmp*"))
+                        ignore=shutil.ignore_patterns("__pycache__", "golden_tmp*", "liboracle_*.so"))
     shutil.copy(os.path.join(ROOT, "pytest.ini"), dst)
 
 
@@ -98,7 +108,7 @@ def _run_pins(dst, pin_file):
 
 def test_unmodified_copy_passes(tmp_path):
     _copy_tree(str(tmp_path))
-    for pin in (STEP, PACK, LOOP, QUOTA, FEAT, SHARD):
+    for pin in (STEP, PACK, LOOP, QUOTA, FEAT, SHARD, ROWS):
         r = _run_pins(str(tmp_path), pin)
         assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
 
