@@ -16,8 +16,9 @@ STATUS_NAMES = {0: "DLLM_OK", 1: "DLLM_ERR_ARG", 2: "DLLM_ERR_SHAPE", 3: "DLLM_E
                 4: "DLLM_ERR_CAPACITY", 5: "DLLM_ERR_HIP"}
 DLLM_FP32, DLLM_BF16 = 0, 1
 MAX_L, MAX_ROWS, MAX_POSITIONS, MAX_QUEUE = 1024, 4096, 262144, 8192
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
-EXPORTS = ("dllm_step", "dllm_step_timed", "dllm_step_score", "dllm_step_score_timed", "dllm_step_decide", "dllm_step_quota", "dllm_step_decide_quota",
+EXPORTS = ("dllm_step", "dllm_step_noalloc", "dllm_step_timed", "dllm_step_score", "dllm_step_score_timed", "dllm_step_decide", "dllm_step_quota", "dllm_step_decide_quota",
            "dllm_step_features", "dllm_step_score_shard", "dllm_step_decide_shards", "dllm_shard_triples_bytes",
            "dllm_step_workspace_bytes", "dllm_pack", "dllm_compact", "dllm_last_error")
 
@@ -61,6 +62,9 @@ def lib():
         L.dllm_step.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                 vp, vp, vp, sz, vp]
         L.dllm_step.restype = i32
+        L.dllm_step_noalloc.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp]
+        L.dllm_step_noalloc.restype = i32
         L.dllm_step_timed.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, sz, vp, vp, vp]
         L.dllm_step_timed.restype = i32

@@ -123,6 +123,30 @@ def dllm_step(logits, input_ids, mask_in, mask_out, threshold, done, accept_len,
     _launch(_lib.lib().dllm_step, args, "dllm_step", events, stream)
 
 
+def dllm_step_noalloc(logits, input_ids, mask_in, mask_out, threshold, done, accept_len, status, p=None, b=None,
+                      conf=None, argmax=None, rows=None, L=None, V=None, pos_stride=None, row_stride=None, stream=None):
+    """dllm_step without a workspace: the library's fixed per-device scratch holds the partials
+    (for callers that cannot allocate; calls on one GPU must not overlap).  See include/dllm.h."""
+    rows, L, V, pos_stride, row_stride = _logits_shape(logits, rows, L, V, pos_stride, row_stride)
+    W = input_ids.shape[-1]
+    _need(input_ids, torch.int32, "input_ids", rows * W)
+    _need(mask_in, torch.uint8, "mask_in", rows * L)
+    _need(mask_out, torch.uint8, "mask_out", rows * L)
+    _need(threshold, torch.float32, "threshold", rows)
+    _need(done, torch.uint8, "done", rows)
+    _need(accept_len, torch.int32, "accept_len", rows)
+    _need(status, torch.int32, "status", 1)
+    for t, dt, nm, n in ((p, torch.int32, "p", rows), (b, torch.int32, "b", rows),
+                         (conf, torch.float32, "conf", rows * L), (argmax, torch.int32, "argmax", rows * L)):
+        if t is not None:
+            _need(t, dt, nm, n)
+    rc = _lib.lib().dllm_step_noalloc(_stream(stream), _ptr(logits), _DT[logits.dtype], pos_stride, row_stride, rows,
+                                      L, V, _ptr(input_ids), W, _ptr(mask_in), _ptr(mask_out), _ptr(threshold),
+                                      _ptr(p), _ptr(b), _ptr(conf), _ptr(argmax), _ptr(done), _ptr(accept_len),
+                                      _ptr(status))
+    _lib.check(rc, "dllm_step_noalloc")
+
+
 def dllm_step_timed(logits, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status, kernel_events,
                     p=None, b=None, conf=None, argmax=None, rows=None, L=None, V=None, pos_stride=None,
                     row_stride=None, stream=None):

@@ -35,7 +35,15 @@
 //
 // This file holds the argument checks and the C entry points; the kernels are in score.hip and
 // decide.hip, their shared definitions in step_common.h.
+#include <mutex>
+
 #include "step_common.h"
+
+// The workspace of dllm_step_noalloc: a fixed device array (one copy per GPU, allocated by the
+// runtime with the code object and held until the process ends).  In host code its name is only a
+// stand-in; the device address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever passed on.
+static __device__ __align__(256) unsigned char scratch[DLLM_NOALLOC_SCRATCH_BYTES];
 
 namespace dllm {
 // decide.hip: launch_decide with an event bound to the deciding kernel's end (nullptr: none)
@@ -121,6 +129,29 @@ dllm_status check_decide(const char *who, int32_t *input_ids, int32_t W, const u
 }
 
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call on each device).
+dllm_status scratch_address(const char *who, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return check_hip(e, who);
+    if (dev < 0 || dev >= kMaxDevices) return fail(DLLM_ERR_ARG, "%s: device %d beyond the %d this library tracks", who,
+                                                   dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+        void *addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return check_hip(e, "dllm_step_noalloc: hipGetSymbolAddress");
+        if (addr == nullptr) return fail(DLLM_ERR_HIP, "%s: no device address for the scratch array", who);
+        g_scratch_addr[dev] = addr;
+    }
+    *out = g_scratch_addr[dev];
+    return DLLM_OK;
+}
+
 }  // namespace
 
 
@@ -148,6 +179,35 @@ extern "C" dllm_status dllm_step(void *stream, const void *logits, int32_t dtype
     rc = launch_score(P, dtype, (hipStream_t)stream);
     if (rc != DLLM_OK) return rc;
     return launch_decide(P, (hipStream_t)stream, P.S > 0 ? kRuleQuota : kRuleThreshold);
+}
+
+extern "C" dllm_status dllm_step_noalloc(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
+                                         int64_t row_stride, int32_t rows, int32_t L, int32_t V, int32_t *input_ids,
+                                         int32_t W, const uint8_t *mask_in, uint8_t *mask_out, const float *threshold,
+                                         const int32_t *p, const int32_t *b, float *conf, int32_t *argmax,
+                                         uint8_t *done, int32_t *accept_len, int32_t *status) {
+    const char *who = "dllm_step_noalloc";
+    StepParams P{};
+    dllm_status rc = check_shape(who, dtype, rows, L, V, nullptr, P);
+    if (rc == DLLM_OK) rc = check_score(who, logits, dtype, pos_stride, row_stride, mask_in, status, P);
+    if (rc == DLLM_OK)
+        rc = check_decide(who, input_ids, W, mask_in, mask_out, threshold, 0, p, b, conf, argmax, done, accept_len,
+                          status, P);
+    if (rc != DLLM_OK || rows == 0) return rc;
+    int NV, NC;
+    size_t need;
+    shape_of(rows, L, V, dtype, NV, NC, need);
+    if (need > DLLM_NOALLOC_SCRATCH_BYTES)
+        return fail(DLLM_ERR_CAPACITY, "%s: rows=%d, L=%d, V=%d need %zu bytes of workspace; the fixed scratch "
+                    "holds %zu (use dllm_step with a caller workspace)", who, rows, L, V, need,
+                    (size_t)DLLM_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    rc = scratch_address(who, &ws);
+    if (rc != DLLM_OK) return rc;
+    P.partials = (float4 *)ws;
+    rc = launch_score(P, dtype, (hipStream_t)stream);
+    if (rc != DLLM_OK) return rc;
+    return launch_decide(P, (hipStream_t)stream, kRuleThreshold);
 }
 
 extern "C" dllm_status dllm_step_timed(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,

@@ -152,6 +152,26 @@ dllm_status dllm_step_timed(void *stream, const void *logits, int32_t dtype, int
  * arguments). */
 size_t dllm_step_workspace_bytes(int32_t rows, int32_t L, int32_t V, int32_t dtype);
 
+/* dllm_step_noalloc — dllm_step for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, and harnesses that forbid hipMalloc.  It takes no workspace
+ * and allocates nothing: its per-chunk partials live in a fixed device array of
+ * DLLM_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held until the process ends; its
+ * address is looked up once per device, on the first call on that device).  Arguments, outputs,
+ * status and errors as for dllm_step, plus DLLM_ERR_CAPACITY, before anything is launched, when the
+ * shape needs more workspace than that (dllm_step_workspace_bytes(rows, L, V, dtype) >
+ * DLLM_NOALLOC_SCRATCH_BYTES: at V = 152064 bf16, rows * L up to 27594 slots fit, so 256 rows of
+ * L = 64 do).  The
+ * array keeps whatever the last call left; the step writes every partial before reading it, so
+ * it needs no clearing.  Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (on different streams, or from different host threads without ordering) race
+ * and give wrong results.  Results are bit for bit those of dllm_step. */
+#define DLLM_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+dllm_status dllm_step_noalloc(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
+                              int64_t row_stride, int32_t rows, int32_t L, int32_t V, int32_t *input_ids,
+                              int32_t W, const uint8_t *mask_in, uint8_t *mask_out, const float *threshold,
+                              const int32_t *p, const int32_t *b, float *conf, int32_t *argmax, uint8_t *done,
+                              int32_t *accept_len, int32_t *status);
+
 /* dllm_step_score and dllm_step_decide — dllm_step in its two halves, for callers that time,
  * overlap or schedule them apart.  Calling dllm_step_score, then dllm_step_decide on the same
  * stream with the same dtype, rows, L, V, mask_in and workspace, equals one dllm_step call

@@ -278,6 +278,8 @@ def test_binding_limits_match_the_header():
     got = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define DLLM_(MAX_\w+)\s+(\d+)", text)}
     assert got["MAX_L"] == _lib.MAX_L and got["MAX_ROWS"] == _lib.MAX_ROWS
     assert got["MAX_POSITIONS"] == _lib.MAX_POSITIONS and got["MAX_QUEUE"] == _lib.MAX_QUEUE
+    m = re.search(r"#define DLLM_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
 
 
 def test_binding_rejects_a_strided_vocabulary():
@@ -292,3 +294,29 @@ def test_binding_rejects_a_strided_vocabulary():
         api._logits_shape(x.reshape(-1)[::2], 2, 3, 16, 16, 48)
     with pytest.raises(ValueError, match="device tensor"):          # a contiguous view passes the stride test
         api._logits_shape(x[..., :8], None, None, None, None, None)
+
+
+def test_noalloc_step_rejects_bad_arguments_and_oversize():
+    """dllm_step_noalloc checks what dllm_step checks, and refuses a shape whose workspace would not
+    fit its fixed scratch array, all before touching a device."""
+    L = _lib.lib()
+
+    def na(**kw):
+        a = dict(logits=FAKE, dtype=1, ps=152064, rs=64 * 152064, rows=256, L=64, V=152064, ids=FAKE, W=5000,
+                 mi=FAKE, mo=ctypes.c_void_p(0x900000), tau=FAKE, done=FAKE, acc=FAKE, status=FAKE)
+        a.update(kw)
+        return L.dllm_step_noalloc(None, a["logits"], a["dtype"], a["ps"], a["rs"], a["rows"], a["L"], a["V"],
+                                   a["ids"], a["W"], a["mi"], a["mo"], a["tau"], None, None, None, None, a["done"],
+                                   a["acc"], a["status"])
+    assert na(dtype=7) == _lib.DLLM_ERR_DTYPE
+    assert na(logits=None) == _lib.DLLM_ERR_ARG
+    assert na(ps=100) == _lib.DLLM_ERR_ARG
+    assert na(W=63) == _lib.DLLM_ERR_SHAPE
+    assert na(tau=None) == _lib.DLLM_ERR_ARG
+    assert na(rows=0, logits=None, ids=None) == _lib.DLLM_OK
+    # the largest batch of the large FDFO run (256 x 64 slots at V = 152064 bf16) fits; 4x as many rows do not
+    assert L.dllm_step_workspace_bytes(256, 64, 152064, 1) <= _lib.NOALLOC_SCRATCH_BYTES
+    big = dict(rows=1024, mo=ctypes.c_void_p(0x4000000))
+    assert L.dllm_step_workspace_bytes(1024, 64, 152064, 1) > _lib.NOALLOC_SCRATCH_BYTES
+    assert na(**big) == _lib.DLLM_ERR_CAPACITY
+    assert "scratch" in _lib.last_error()
