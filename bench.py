@@ -10,9 +10,10 @@ dllm_compact (scatter, commit, evict).  Every step starts from its own pristine 
 state, and the logits rotate over several device buffers (more bytes than the 256 MB Infinity
 Cache), all resident in HBM before timing.
 
-Reports masked positions scored per second over the timed region, the HBM roofline fraction of
-the scoring kernel (the dominant one) from HIP events on the launch stream, and the float64
-oracle's rate on the host cores (run first, before the GPU is touched).
+Reports masked positions scored per second over the timed region; the HBM roofline fraction of the
+whole dllm_step (scoring kernel start to deciding kernel end) with the scoring kernel's own beside
+it, from kernel-bound HIP events on the launch stream over steps run right after the timed region;
+and the float64 oracle's rate on the host cores (run first, before the GPU is touched).
 
 Other modes: --step large-fdfo times the same path on the largest single batch (256 requests at
 block 0, L=64, V=152064, every slot masked: 4.98 GB of logits per step); --copy-calibration MIB
@@ -43,7 +44,7 @@ SCORE_SRC = [os.path.join(ROOT, "confidence_block_unmasking_amd", "csrc", f) for
             [os.path.join(ROOT, "include", "dllm.h")]
 SCORE_KERNEL = "score_kernel"
 COPY_MIB = 256
-EV_EVERY = 16         # steps between two HIP-event timings of the scoring kernel
+SAMPLES = 50          # event-timed steps of each kind after the timed region
 DEFAULT_STEP = "dream-dynamic-step"
 STEP_WORKLOADS = {
     "dream-dynamic-step": "Dream-shaped dynamic-threshold step: 64 requests, L=32, V=152064 bf16 logits, "
@@ -273,7 +274,11 @@ def run_gpu(args):
         synth.logits_gpu(t, w.dtype, rows, L, V, rr, bb, mm, w.logit_seed + 7919 * k, w.sigma, w.umax)
         bufs.append(t)
     n_total = args.warmup + args.steps
-    copies = [_Copy(sess) for _ in range(n_total)]
+    # after the timed steps, a few untimed ones, then 2 * args.samples more of the same kind, each
+    # timed by HIP events (the scoring kernel or the whole dllm_step), outside the wall-clock region
+    n_settle = 2 * args.rotate          # untimed steps between the timed region and the sampled ones
+    n_all = n_total + n_settle + 2 * args.samples
+    copies = [_Copy(sess) for _ in range(n_all)]
     torch.cuda.synchronize()
 
     lib = _lib.lib()
@@ -319,30 +324,24 @@ def run_gpu(args):
         comp_args.append((stream, rows, L, W, w.mask_id, -1, P(box), P(mask_b), P(sess.done), P(c.row_req),
                           w.rows_cap, ctypes.byref(c.reqs), ctypes.byref(c.queue), w.budget, P(c.meta),
                           P(sess.status)))
-    # HIP events on the launch stream (torch's current stream) for the scoring kernel of every
-    # --ev-every-th step: timing costs the stream some microseconds, so timing every step would
-    # inflate the step time that `value` is computed from.  The events are bound to the kernel's own
-    # start and end (dllm_step_score_timed); the vocabulary-shard mode, which has no timed variant,
-    # records a pair around the first shard's call instead (that also holds the dispatch latency)
-    # the sampled steps cycle through the logits buffers (step k reads buffer k % rotate), so that
-    # every buffer is timed, not only the one that a stride dividing `rotate` would always land on
-    def _sample(i):
-        if args.rotate > args.ev_every:
-            return i * args.ev_every
-        return i * args.ev_every + (i % args.rotate - i * args.ev_every) % args.rotate   # buffer i % rotate
-    samples = [_sample(i) for i in range(n_total // args.ev_every + 1)]
-    samples = [k for k in samples if k < n_total]
-    if not any(k >= args.warmup for k in samples):
-        raise SystemExit("no timed step carries a timing of the scoring kernel: lower --ev-every")
-    kev = {k: api.KernelEvents() for k in samples} if args.shards <= 1 else {}
+    # Timing.  The timed region carries no events: each costs the stream some microseconds, which
+    # would inflate the step time `value` comes from.  Right after it, on the same state, come
+    # 2 * args.samples steps of the same kind, each with one pair of HIP events on the launch stream
+    # (torch's current stream), in alternating runs of one step per logits buffer: bound to the
+    # scoring kernel's start and end (dllm_step_score_timed), or to the scoring kernel's start and
+    # the deciding kernel's end (dllm_step_timed: the whole dllm_step).  So both kinds read every
+    # logits buffer.  The vocabulary-shard mode, which has no bound variant, records a pair around the first
+    # shard's call instead (that also holds the dispatch latency); the quota rule times only the
+    # scoring kernel.
+    samp = list(range(n_total + n_settle, n_all))
+    # alternate in runs of `rotate` steps, so that both kinds read every logits buffer
+    score_k = [k for i, k in enumerate(samp)
+               if (i // args.rotate) % 2 == 0 or args.shards > 1 or args.rule != "threshold"]
+    step_k = [k for k in samp if k not in score_k]
+    kev = {k: api.KernelEvents() for k in score_k} if args.shards <= 1 else {}
     ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for k in samples} if args.shards > 1 else {}
-    # half a stride later, the whole dllm_step (threshold rule) is timed the same way: from the
-    # scoring kernel's start to the deciding kernel's end (dllm_step_timed)
-    half = args.ev_every // 2
-    sev = {k + half: api.KernelEvents() for k in samples
-           if half > 0 and k + half < n_total and k + half not in kev} \
-        if args.shards <= 1 and args.rule == "threshold" else {}
+          for k in score_k} if args.shards > 1 else {}
+    sev = {k: api.KernelEvents() for k in step_k}
 
     def one(k):
         rc = lib.dllm_pack(*pack_args[k])
@@ -379,6 +378,9 @@ def run_gpu(args):
         rc |= one(k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    for k in range(n_total, n_all):        # a few untimed steps first: the stream is busy again
+        rc |= one(k)                       # before the first sampled launch
+    torch.cuda.synchronize()
     if rc != 0 or int(sess.status.item()) != 0:
         raise SystemExit(f"library error rc={rc} status={int(sess.status.item())}: {_lib.last_error()}")
     metas = {bytes(c.meta.cpu().numpy()) for c in copies[args.warmup:]}
@@ -421,19 +423,37 @@ def run_gpu(args):
                             "dllm_step_score + dllm_step_decide between two HIP events recorded around the calls") +
                            ", each launch after a 1 GiB write that evicts L2 and the Infinity Cache"}
         del flush
-    timed_k = [k for k in samples if k >= args.warmup]
     if kev:
-        kern_ms = np.array([kev[k].elapsed_ms() for k in timed_k])
+        kern_ms = np.array([kev[k].elapsed_ms() for k in score_k])
     else:
-        kern_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in timed_k])
+        kern_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in score_k])
     by_buf = {}
-    for k, t in zip(timed_k, kern_ms):
+    for k, t in zip(score_k, kern_ms):
         by_buf.setdefault(k % args.rotate, []).append(float(t) * 1e3)
-    kern_s = float(kern_ms.mean()) / 1e3
-    step_ms = np.array([sev[k].elapsed_ms() for k in sorted(sev) if k >= args.warmup])
+    step_ms = np.array([sev[k].elapsed_ms() for k in step_k])
     step_bytes = M * V * 2
     timed_bytes = step_bytes if args.shards <= 1 else M * (V // args.shards) * 2
-    achieved = timed_bytes / kern_s / 1e9
+
+    def dist(ms):
+        us = ms * 1e3
+        return {"samples": int(us.size), "mean": float(us.mean()), "p10": float(np.percentile(us, 10)),
+                "p50": float(np.percentile(us, 50)), "p90": float(np.percentile(us, 90))}
+    kern_achieved = timed_bytes / (float(kern_ms.mean()) * 1e-3) / 1e9
+    traffic = (stored_traffic(M) if args.shards <= 1 and args.rule == "threshold" and args.step == DEFAULT_STEP
+               else None)
+    score_roof = {"kernel": "score_kernel", "achieved": kern_achieved, "frac": kern_achieved / PEAK_HBM_GBPS,
+                  "samples": int(kern_ms.size), "traffic": traffic}
+    if step_ms.size:
+        # the whole dllm_step (scoring kernel, launch boundary, deciding kernel) against the bytes the
+        # step must read; the scoring kernel's own fraction beside it
+        achieved = step_bytes / (float(step_ms.mean()) * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "dllm_step (score_kernel start to decide_kernel end)",
+                    "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                    "traffic": traffic, "samples": int(step_ms.size), "score_kernel": score_roof}
+    else:
+        roofline = {"bound": "hbm", "kernel": "score_kernel", "achieved": kern_achieved, "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": kern_achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                    "samples": int(kern_ms.size)}
     return {
         "metric": METRIC,
         "value": M * args.steps / elapsed,
@@ -454,25 +474,19 @@ def run_gpu(args):
                    "requests": rows, "block_len": L, "vocab": V, "logits_dtype": "bf16",
                    "masked_positions_per_step": M, "box_width": W, "logits_buffers": args.rotate},
         "logits_GBps": step_bytes * args.steps / elapsed / 1e9,
-        "score_kernel_us": {"samples": int(kern_ms.size), "mean": float(kern_ms.mean()) * 1e3,
-                            "p10": float(np.percentile(kern_ms, 10)) * 1e3,
-                            "p50": float(np.percentile(kern_ms, 50)) * 1e3,
-                            "p90": float(np.percentile(kern_ms, 90)) * 1e3,
+        "score_kernel_us": {**dist(kern_ms),
                             "by_logits_buffer": [round(float(np.mean(by_buf[b])), 2) if b in by_buf else None
                                                  for b in range(args.rotate)],
                             "what": ("HIP events bound to the kernel's start and end (dllm_step_score_timed)"
-                                     if kev else "HIP events recorded around the call")},
-        **({"dllm_step_us": {"samples": int(step_ms.size), "mean": float(step_ms.mean()) * 1e3,
-                             "p50": float(np.percentile(step_ms, 50)) * 1e3,
+                                     if kev else "HIP events recorded around the call") +
+                                    ", on steps run right after the timed region"},
+        **({"dllm_step_us": {**dist(step_ms),
                              "frac_of_peak_at_mean": step_bytes / (float(step_ms.mean()) * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                             "what": "dllm_step (score + decide) inside the timed loop, from the scoring kernel's "
-                                     "start to the deciding kernel's end (dllm_step_timed), half a stride after "
-                                     "each scoring-kernel timing"}} if step_ms.size else {}),
+                             "what": "dllm_step (score + decide) from the scoring kernel's start to the deciding "
+                                     "kernel's end (dllm_step_timed), on steps run right after the timed region"}}
+           if step_ms.size else {}),
         **({"dllm_step_cold_us": cold_us} if cold_us else {}),
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": (stored_traffic(M) if args.shards <= 1 and args.rule == "threshold"
-                                 and args.step == DEFAULT_STEP else None)},
+        "roofline": roofline,
         **({"timed_kernel": f"dllm_step_score_shard of shard 0 of {args.shards} (scoring + per-slot shard record)"}
            if args.shards > 1 else {}),
     }
@@ -521,7 +535,8 @@ def main():
     ap.add_argument("--step", choices=tuple(STEP_WORKLOADS), default=DEFAULT_STEP,
                     help="the batch one timed step processes (the default is the headline workload)")
     ap.add_argument("--rotate", type=int, default=4, help="logits buffers cycled through")
-    ap.add_argument("--ev-every", type=int, default=EV_EVERY, help="steps between two timings of the scoring kernel")
+    ap.add_argument("--samples", type=int, default=SAMPLES,
+                    help="event-timed steps of each kind (scoring kernel, whole dllm_step) after the timed region")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU work of the oracle baseline, in all")
     ap.add_argument("--rule", choices=("threshold", "quota"), default="threshold",
                     help="unmasking rule: LowConfidence threshold (default) or the fixed per-step quota")
@@ -545,8 +560,8 @@ def main():
         print(f"bench.py: the step runs on one GPU only (asked for --gpus {args.gpus}); its rows would shard "
               "across GPUs without any exchange, but no multi-GPU launcher is provided", file=sys.stderr)
         sys.exit(2)
-    if args.ev_every < 1 or args.ev_every > args.steps:
-        raise SystemExit("--ev-every must lie in [1, --steps], so that a timed step carries a timing")
+    if args.samples < 1:
+        raise SystemExit("--samples must be at least 1")
     if args.record_traffic:
         from workload import configs
         w = configs.dream_step()
