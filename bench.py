@@ -299,7 +299,7 @@ def run_gpu(args):
         decide_fn = lib.dllm_step_decide
         decide_args = (stream, _lib.DLLM_BF16, rows, L, V, P(box), W, P(mask_a), P(mask_b), P(sess.tau),
                        P(sess.p_rows), P(sess.b_rows), P(sess.conf), P(sess.argmax), P(sess.done), P(sess.accept), ws,
-                       wsn, P(sess.status))
+                       wsn, P(sess.status), None, None)
     if args.shards > 1:
         # vocabulary split into args.shards contiguous slices, scored one after the other (what each
         # rank of a tensor-parallel group would do with its own slice), then combined and decided
@@ -359,7 +359,7 @@ def run_gpu(args):
             rc |= lib.dllm_step_score_timed(*score_args[k % args.rotate], kev[k].start, kev[k].stop)
         elif k in sev:
             sa = score_args[k % args.rotate]
-            rc |= lib.dllm_step_timed(*sa[:8], *decide_args[5:], sev[k].start, sev[k].stop)
+            rc |= lib.dllm_step_timed(*sa[:8], *decide_args[5:19], sev[k].start, sev[k].stop)
         else:
             rc |= lib.dllm_step_score(*score_args[k % args.rotate])
         if k not in sev:
@@ -401,7 +401,7 @@ def run_gpu(args):
                 # kernel's end (the arguments of the two halves, in dllm_step's order)
                 e = api.KernelEvents()
                 sa, da = score_args[k % args.rotate], decide_args
-                rc |= lib.dllm_step_timed(*sa[:8], *da[5:], e.start, e.stop)
+                rc |= lib.dllm_step_timed(*sa[:8], *da[5:19], e.start, e.stop)
             else:
                 e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 e[0].record()

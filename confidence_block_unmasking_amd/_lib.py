@@ -73,7 +73,7 @@ def lib():
         L.dllm_step_score_timed.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, vp, sz, vp, vp, vp]
         L.dllm_step_score_timed.restype = i32
         L.dllm_step_decide.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                       vp, sz, vp]
+                                       vp, sz, vp, vp, vp]
         L.dllm_step_decide.restype = i32
         L.dllm_step_quota.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp,
                                       vp, vp, vp, vp, sz, vp]

@@ -215,17 +215,23 @@ def dllm_step_score_timed(logits, mask_in, workspace, status, events, rows=None,
 
 
 def dllm_step_decide(dtype, rows, L, V, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status,
-                     p=None, b=None, conf=None, argmax=None, stream=None):
+                     p=None, b=None, conf=None, argmax=None, unmasked=None, fallback=None, stream=None, events=None):
     """The deciding half of dllm_step, on the partials dllm_step_score left in `workspace`
-    (same dtype, rows, L, V and mask_in)."""
+    (same dtype, rows, L, V and mask_in).  unmasked (int32 [rows]) and fallback (uint8 [rows]),
+    when given, receive each row's count of slots unmasked and whether the rule's single-slot
+    fallback applied.  events: optional pair of timing events recorded right around the call."""
     if dtype not in _DT:
         raise ValueError(f"dtype {dtype} not supported")
     W = _decide_args(rows, L, input_ids, mask_in, mask_out, threshold, done, accept_len, workspace, status, p, b,
                      conf, argmax)
-    rc = _lib.lib().dllm_step_decide(_stream(stream), _DT[dtype], rows, L, V, _ptr(input_ids), W, _ptr(mask_in),
-                                     _ptr(mask_out), _ptr(threshold), _ptr(p), _ptr(b), _ptr(conf), _ptr(argmax),
-                                     _ptr(done), _ptr(accept_len), _ptr(workspace), workspace.numel(), _ptr(status))
-    _lib.check(rc, "dllm_step_decide")
+    if unmasked is not None:
+        _need(unmasked, torch.int32, "unmasked", rows)
+    if fallback is not None:
+        _need(fallback, torch.uint8, "fallback", rows)
+    args = (_stream(stream), _DT[dtype], rows, L, V, _ptr(input_ids), W, _ptr(mask_in), _ptr(mask_out),
+            _ptr(threshold), _ptr(p), _ptr(b), _ptr(conf), _ptr(argmax), _ptr(done), _ptr(accept_len),
+            _ptr(workspace), workspace.numel(), _ptr(status), _ptr(unmasked), _ptr(fallback))
+    _launch(_lib.lib().dllm_step_decide, args, "dllm_step_decide", events, stream)
 
 
 def dllm_step_quota(logits, input_ids, mask_in, mask_out, steps_per_block, done, accept_len, workspace, status,

@@ -205,6 +205,8 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepParams P) {
         const bool fin = nmasked == n_unmasked;
         P.done[row] = fin ? 1 : 0;
         P.accept[row] = fin ? L : 0;
+        if (P.unmasked_out) P.unmasked_out[row] = n_unmasked;
+        if (P.fallback_out) P.fallback_out[row] = (!QUOTA && nmasked > 0 && !any_above) ? 1 : 0;
     }
 }
 

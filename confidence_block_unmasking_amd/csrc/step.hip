@@ -260,7 +260,8 @@ extern "C" dllm_status dllm_step_decide(void *stream, int32_t dtype, int32_t row
                                         int32_t *input_ids, int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
                                         const float *threshold, const int32_t *p, const int32_t *b, float *conf,
                                         int32_t *argmax, uint8_t *done, int32_t *accept_len, void *workspace,
-                                        size_t workspace_bytes, int32_t *status) {
+                                        size_t workspace_bytes, int32_t *status, int32_t *unmasked,
+                                        uint8_t *fallback) {
     StepParams P{};
     dllm_status rc = check_shape("dllm_step_decide", dtype, rows, L, V, workspace, P);
     if (rc == DLLM_OK)
@@ -268,6 +269,8 @@ extern "C" dllm_status dllm_step_decide(void *stream, int32_t dtype, int32_t row
                           done, accept_len, status, P);
     if (rc == DLLM_OK) rc = check_workspace("dllm_step_decide", dtype, workspace, workspace_bytes, P);
     if (rc != DLLM_OK || rows == 0) return rc;
+    P.unmasked_out = unmasked;
+    P.fallback_out = fallback;
     return launch_decide(P, (hipStream_t)stream, P.S > 0 ? kRuleQuota : kRuleThreshold);
 }
 

@@ -44,6 +44,8 @@ struct StepParams {
     int32_t *arg_out;
     uint8_t *done;
     int32_t *accept;
+    int32_t *unmasked_out;                    // per row: slots unmasked (optional)
+    uint8_t *fallback_out;                    // per row: the rule's single-slot fallback applied (optional)
     float4 *partials;                         // [rows*L*NC] {max, sum, element index, -}
     int32_t *status;
 };

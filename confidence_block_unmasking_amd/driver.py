@@ -70,6 +70,9 @@ class Session:
         self.status = torch.zeros(1, dtype=i32, device=device)
         self.meta = torch.zeros(32, dtype=u8, device=device)
         self.features_buf = torch.empty(n * api.N_FEATURES, dtype=f32, device=device)
+        # per-row report of the last step (metrics runs): slots unmasked, single-slot fallback taken
+        self.unmasked_rows = torch.zeros(n, dtype=i32, device=device)
+        self.fallback_rows = torch.zeros(n, dtype=u8, device=device)
         # pinned host copies for the per-step read-back (done, new mask and status in one sync)
         pin = str(device).startswith("cuda")
         self._h_done = torch.empty(n, dtype=u8, pin_memory=pin)
@@ -153,12 +156,25 @@ class Session:
             events=ev))
         self.stats["packs"] += 1
 
-    def step(self, timed=False):
+    def step(self, timed=False, report=False):
+        """One dllm_step on the current box.  report=True runs it as its two halves, the deciding one
+        also writing each row's count of unmasked slots and fallback flag (unmasked_rows,
+        fallback_rows); the results are the same bit for bit."""
         nxt = 1 - self.cur
-        self._timed("step", timed, lambda ev: api.dllm_step(
-            self.logits, self.box(), self.masks[self.cur], self.masks[nxt], self.tau, self.done, self.accept,
-            self.workspace, self.status, p=self.p_rows, b=self.b_rows, conf=self.conf, argmax=self.argmax,
-            rows=self.rows, L=self.L, V=self.V, pos_stride=self.V, row_stride=self.L * self.V, events=ev))
+        if report:
+            def both(ev):
+                api.dllm_step_score(self.logits, self.masks[self.cur], self.workspace, self.status, rows=self.rows,
+                                    L=self.L, V=self.V, pos_stride=self.V, row_stride=self.L * self.V)
+                api.dllm_step_decide(self.dtype, self.rows, self.L, self.V, self.box(), self.masks[self.cur],
+                                     self.masks[nxt], self.tau, self.done, self.accept, self.workspace, self.status,
+                                     p=self.p_rows, b=self.b_rows, conf=self.conf, argmax=self.argmax,
+                                     unmasked=self.unmasked_rows, fallback=self.fallback_rows)
+            self._timed("step", timed, lambda ev: _around(ev, lambda: both(ev)))
+        else:
+            self._timed("step", timed, lambda ev: api.dllm_step(
+                self.logits, self.box(), self.masks[self.cur], self.masks[nxt], self.tau, self.done, self.accept,
+                self.workspace, self.status, p=self.p_rows, b=self.b_rows, conf=self.conf, argmax=self.argmax,
+                rows=self.rows, L=self.L, V=self.V, pos_stride=self.V, row_stride=self.L * self.V, events=ev))
         self.cur = nxt
 
     def features(self):
@@ -179,9 +195,10 @@ class Session:
         new mask) — the test harness uses it to check each step.  timed: bracket every forward,
         step, pack and compact with events (totals from phase_ms()).  max_rounds > 0 returns after
         that many scheduler rounds, right after a compact, where snapshot() holds the whole state.
-        The stats always count the tokens unmasked; metrics=True also reads back the confidences and
-        the row map to count the row-steps decided by the fallback (no masked confidence above the
-        threshold) and the steps each finished block took (stats["block_steps"]: steps -> blocks).
+        The stats always count the tokens unmasked; metrics=True also reads back the step's per-row
+        fallback flags (dllm_step_decide's report: no masked confidence above the threshold) and the
+        row map, to count the fallback row-steps and the steps each finished block took
+        (stats["block_steps"]: steps -> blocks).
         Returns self.stats."""
         assert mode in ("sync", "fdfo", "handback")
         self.compact(with_box=False, timed=timed)    # admission at the start of the run
@@ -190,7 +207,6 @@ class Session:
             self.pack(timed=timed)
             mask_host = self.mask().cpu().numpy()
             if metrics:
-                tau_host = self.tau[:self.rows].cpu().numpy()
                 req_host = self.row_req[:self.rows].cpu().numpy()
             while True:
                 if self.stats["steps"] >= max_steps:
@@ -201,7 +217,7 @@ class Session:
                 self.stats["idle_request_steps"] += int((~masked_rows).sum())
                 self.stats["positions_scored"] += int(masked.sum())
                 self._timed("forward", timed, lambda ev: _around(ev, lambda: forward(self)))
-                self.step(timed=timed)
+                self.step(timed=timed, report=metrics)
                 done, mask_host, st = self._readback()
                 if st != 0:
                     raise api.DllmError(st, "dllm_step", "(device status)")
@@ -209,9 +225,7 @@ class Session:
                 unmasked = int(masked.sum()) - int((mask_host != 0).sum())
                 self.stats["unmasked"] += unmasked
                 if metrics:
-                    conf = self.conf[:self.rows * self.L].view(self.rows, self.L).cpu().numpy()
-                    above = (masked & (conf > tau_host[:, None])).any(axis=1)
-                    self.stats["fallback_row_steps"] += int((masked_rows & ~above).sum())
+                    self.stats["fallback_row_steps"] += int(self.fallback_rows[:self.rows].sum().item())
                     for r in np.flatnonzero(masked_rows):
                         q = int(req_host[r])
                         in_block[q] = in_block.get(q, 0) + 1

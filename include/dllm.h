@@ -182,7 +182,12 @@ dllm_status dllm_step_noalloc(void *stream, const void *logits, int32_t dtype, i
  * predicted) to per-chunk partial results (max, sum of exp(x - max), first index at the max) in
  * the workspace.  Arguments as for dllm_step; writes only the workspace (and *status).
  * dllm_step_decide: merges those partials in a fixed order into conf and argmax and applies the
- * LowConfidence rule, with the outputs and conditions of dllm_step.  It reads no logits.
+ * LowConfidence rule, with the outputs and conditions of dllm_step.  It reads no logits.  Two
+ * optional per-row outputs (device arrays of `rows` entries, or NULL) report how the rule went,
+ * the per-request result of a step ([FDFO] §工程设计二) beside the accept length:
+ *   unmasked[r] (int32) = the number of slots the step unmasked in row r;
+ *   fallback[r] (uint8) = 1 if row r had masked slots and none exceeded its threshold (so the
+ *   single most confident one was unmasked), else 0.
  * Errors: those of dllm_step that concern each half's own arguments. */
 dllm_status dllm_step_score(void *stream, const void *logits, int32_t dtype, int64_t pos_stride,
                             int64_t row_stride, int32_t rows, int32_t L, int32_t V, const uint8_t *mask_in,
@@ -201,7 +206,7 @@ dllm_status dllm_step_decide(void *stream, int32_t dtype, int32_t rows, int32_t 
                              int32_t *input_ids, int32_t W, const uint8_t *mask_in, uint8_t *mask_out,
                              const float *threshold, const int32_t *p, const int32_t *b, float *conf,
                              int32_t *argmax, uint8_t *done, int32_t *accept_len, void *workspace,
-                             size_t workspace_bytes, int32_t *status);
+                             size_t workspace_bytes, int32_t *status, int32_t *unmasked, uint8_t *fallback);
 
 /* dllm_step_quota and dllm_step_decide_quota — the step (and its deciding half) with the fixed
  * per-step quota of [BlockServe] §II-E (向量化混合调度执行: the per-step transfer quota spreads a

@@ -52,25 +52,27 @@ def score(x: np.ndarray):
     return m, a, S, 1.0 / S
 
 
-def decide(conf: np.ndarray, masked: np.ndarray, tau) -> np.ndarray:
+def decide(conf: np.ndarray, masked: np.ndarray, tau, return_fallback: bool = False):
     """LowConfidence unmask set for one row's active block.
 
     conf: float64 [L] confidences (only masked entries are looked at); masked: bool [L];
     tau: the request's threshold as stored (float32), compared in float64.
     Returns bool [L]: U = {masked j : conf_j > tau}; if U is empty while some slot is masked,
-    U = {the masked j with the largest conf, lowest j on ties}.
+    U = {the masked j with the largest conf, lowest j on ties}.  With return_fallback, also
+    whether that second case (the fallback) applied.
     Readings: "exceeds" is strict (>); the fallback is per row and unmasks exactly one slot.
     """
     masked = np.asarray(masked, bool)
     t = float(np.float32(tau))
     U = masked & (np.asarray(conf, np.float64) > t)
-    if not U.any() and masked.any():
+    fallback = not U.any() and masked.any()
+    if fallback:
         best_j, best_c = -1, -np.inf
         for j in range(len(masked)):           # ascending j, strict >: the lowest j wins ties
             if masked[j] and conf[j] > best_c:
                 best_j, best_c = j, conf[j]
         U[best_j] = True
-    return U
+    return (U, fallback) if return_fallback else U
 
 
 def step(logits, dtype: str, input_ids: np.ndarray, mask: np.ndarray, threshold: np.ndarray,
@@ -84,7 +86,9 @@ def step(logits, dtype: str, input_ids: np.ndarray, mask: np.ndarray, threshold:
     conf_override: optional float64 [rows, L]; when given, the rule is applied to these
     confidences instead of the oracle's own (used to replay a decision taken elsewhere).
     Returns a dict with new ids, mask, done (uint8 [rows]), accept (int32 [rows]), conf (float64
-    [rows, L], -1 where not scored), argmax (int64 [rows, L], -1 where not scored), unmask (bool).
+    [rows, L], -1 where not scored), argmax (int64 [rows, L], -1 where not scored), unmask (bool),
+    unmasked (int32 [rows]: slots unmasked this step) and fallback (uint8 [rows]: 1 where the row
+    had masked slots and none exceeded its threshold, so the single most confident one was taken).
     Reading: a row that enters with no masked slot is left unchanged and reports done=1, accept=L.
     """
     rows, L = mask.shape
@@ -96,6 +100,8 @@ def step(logits, dtype: str, input_ids: np.ndarray, mask: np.ndarray, threshold:
     done = np.zeros(rows, np.uint8)
     accept = np.zeros(rows, np.int32)
     unmask = np.zeros((rows, L), bool)
+    unmasked = np.zeros(rows, np.int32)
+    fallback = np.zeros(rows, np.uint8)
     for r in range(rows):
         if p is not None and b is not None and int(p[r]) + (int(b[r]) + 1) * L > W:
             raise ValueError(f"row {r} does not fit the box")
@@ -106,12 +112,15 @@ def step(logits, dtype: str, input_ids: np.ndarray, mask: np.ndarray, threshold:
                 conf[r, j] = c
                 arg[r, j] = a
         use = conf[r] if conf_override is None else np.asarray(conf_override[r], np.float64)
-        U = decide(use, masked, threshold[r])
+        U, fb = decide(use, masked, threshold[r], return_fallback=True)
         unmask[r] = U
+        unmasked[r] = int(U.sum())
+        fallback[r] = 1 if fb else 0
         for j in range(L):
             if U[j]:
                 ids[r, W - L + j] = arg[r, j]
                 new_mask[r, j] = 0
         done[r] = 1 if not (new_mask[r] != 0).any() else 0
         accept[r] = L if done[r] else 0
-    return dict(ids=ids, mask=new_mask, done=done, accept=accept, conf=conf, argmax=arg, unmask=unmask)
+    return dict(ids=ids, mask=new_mask, done=done, accept=accept, conf=conf, argmax=arg, unmask=unmask,
+                unmasked=unmasked, fallback=fallback)

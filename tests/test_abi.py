@@ -95,7 +95,8 @@ def test_step_halves_reject_bad_arguments():
                  acc=f, ws=ws, n=need, status=f)
         a.update(kw)
         return L.dllm_step_decide(None, a["dtype"], a["rows"], a["L"], a["V"], a["ids"], a["W"], a["mi"], a["mo"],
-                                  a["tau"], None, None, None, None, a["done"], a["acc"], a["ws"], a["n"], a["status"])
+                                  a["tau"], None, None, None, None, a["done"], a["acc"], a["ws"], a["n"], a["status"],
+                                  None, None)
     assert score(dtype=5) == _lib.DLLM_ERR_DTYPE
     assert score(logits=None) == _lib.DLLM_ERR_ARG
     assert score(ps=100) == _lib.DLLM_ERR_ARG

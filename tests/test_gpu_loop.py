@@ -115,7 +115,7 @@ def lockstep_run(w, full_score_max=64, sample=16, whole_rows=1, deep_every=1, se
             ids_o, mask_o = pk["box_ids"].copy(), pk["mask"].copy()
             while True:
                 fwd(sess)
-                sess.step()
+                sess.step(report=True)
                 n_steps += 1
                 g_ids = sess.box().cpu().numpy()
                 g_mask = sess.mask().cpu().numpy()
@@ -123,16 +123,21 @@ def lockstep_run(w, full_score_max=64, sample=16, whole_rows=1, deep_every=1, se
                 g_acc = sess.accept[:rows].cpu().numpy()
                 g_conf = sess.conf[:rows * L].view(rows, L).cpu().numpy()
                 g_arg = sess.argmax[:rows * L].view(rows, L).cpu().numpy()
+                g_unm = sess.unmasked_rows[:rows].cpu().numpy()
+                g_fb = sess.fallback_rows[:rows].cpu().numpy()
                 assert int(sess.status.item()) == 0
                 masked = mask_o != 0
                 M = int(masked.sum())
                 n_scored += M
                 U_all = masked & (g_mask == 0)
                 n_unmasked += int(U_all.sum())
-                # (iii) on every row: the GPU's decision is the rule on its own confidences
+                # (iii) on every row: the GPU's decision, and its report of it, are the rule on its own
+                # confidences
                 for r in range(rows):
-                    assert np.array_equal(U_all[r], ostep.decide(g_conf[r].astype(np.float64), masked[r],
-                                                                 pk["threshold"][r])), f"row {r}: rule (iii)"
+                    own, fb = ostep.decide(g_conf[r].astype(np.float64), masked[r], pk["threshold"][r],
+                                           return_fallback=True)
+                    assert np.array_equal(U_all[r], own), f"row {r}: rule (iii)"
+                    assert g_unm[r] == int(own.sum()) and g_fb[r] == int(fb), f"row {r}: unmasked / fallback"
                     assert np.all(g_arg[r][~masked[r]] == -1)
                 if deferred:
                     # every unmasked slot, or every scored slot on the chosen steps, by the C oracle

@@ -406,3 +406,55 @@ def test_workspace_reused_across_shapes():
         g = gpu_step(logits, "bf16", ids, mask, tau, ws=ws)
         check_step(logits, "bf16", ids, mask, tau, g)
     assert CONF_TOL == 1e-5
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_decide_reports_unmasked_and_fallback(case):
+    """dllm_step_decide's per-row report: the slots it unmasked and whether the single-slot fallback
+    applied, against the oracle's (the Dream-shaped step, then random boxes with thresholds 0.5..1
+    where some rows fall back and some have no masked slot)."""
+    from confidence_block_unmasking_amd import api
+    from tests.parity import ambiguous_row
+    rng = np.random.default_rng(900 + case)
+    if case == 0:
+        w = configs.dream_step()
+        pk, logits = _packed_step_inputs(w)
+        ids, mask, tau, dtype = pk["box_ids"], pk["mask"], pk["threshold"], w.dtype
+    else:
+        rows, L, V = int(rng.integers(1, 40)), int(rng.choice([4, 16, 32, 64])), int(rng.integers(50, 3000))
+        logits, ids, mask, tau = _rand_case(rng, rows, L, V, "fp32", p_mask=float(rng.uniform(0.1, 0.9)))
+        tau = rng.choice([0.5, 0.9, 0.99, 1.0], rows).astype(np.float32)
+        mask[0] = 0
+        dtype = "fp32"
+    rows, L, V = logits.shape
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    lg = _to_dev_logits(logits, dtype)
+    d_ids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    d_mask = torch.from_numpy(mask.astype(np.uint8)).cuda()
+    mout = torch.empty_like(d_mask)
+    d_tau = torch.from_numpy(np.asarray(tau, np.float32)).cuda()
+    done = torch.empty(rows, dtype=torch.uint8, device="cuda")
+    acc = torch.empty(rows, dtype=torch.int32, device="cuda")
+    conf = torch.empty((rows, L), dtype=torch.float32, device="cuda")
+    unm = torch.full((rows,), -3, dtype=torch.int32, device="cuda")
+    fb = torch.full((rows,), 7, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = api.new_workspace(rows, L, V, tdt)
+    api.dllm_step_score(lg, d_mask, ws, status)
+    api.dllm_step_decide(tdt, rows, L, V, d_ids, d_mask, mout, d_tau, done, acc, ws, status, conf=conf,
+                         unmasked=unm, fallback=fb)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    g_unm, g_fb, g_conf = unm.cpu().numpy(), fb.cpu().numpy(), conf.cpu().numpy().astype(np.float64)
+    o = ostep.step(logits, dtype, ids, mask, tau)
+    n_amb = 0
+    for r in range(rows):
+        masked = mask[r] != 0
+        own, own_fb = ostep.decide(g_conf[r], masked, tau[r], return_fallback=True)
+        assert g_unm[r] == int(own.sum()) and g_fb[r] == int(own_fb), r
+        if ambiguous_row(o["conf"][r], masked, tau[r]):
+            n_amb += 1
+            continue
+        assert g_unm[r] == o["unmasked"][r] and g_fb[r] == o["fallback"][r], r
+    assert g_fb[0] == 0 and g_unm[0] == 0 or case == 0
+    print(f"case {case}: rows {rows}, fallback rows {int(g_fb.sum())}, ambiguous {n_amb}", flush=True)

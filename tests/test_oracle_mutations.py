@@ -80,6 +80,8 @@ MUTATIONS = [
     ("oracle/features.py", "threshold[r], int(b[r]), int(K[r]), L)", "threshold[r], int(b[0]), int(K[r]), L)", FEAT),
     ("oracle/features.py", "threshold[r], int(b[r]), int(K[r]), L)", "threshold[r], int(b[r]), int(K[-1]), L)", FEAT),
     ("oracle/features.py", "row_features(conf[r], mask_after[r],", "row_features(conf[r], mask_after[0],", FEAT),
+    ("oracle/step.py", "    fallback = not U.any() and masked.any()\n", "    fallback = not U.any()\n", STEP),
+    ("oracle/step.py", "        unmasked[r] = int(U.sum())", "        unmasked[r] = int(masked.sum())", STEP),
     # the C row scorer (rebuilt from the planted source in the scratch copy)
     ("oracle/rows.c", "S += exp(buf[v] - m);", "S += exp(m - buf[v]);", ROWS),
     ("oracle/rows.c", "for (int64_t v = 0; v < V; ++v) S += exp", "for (int64_t v = 1; v < V; ++v) S += exp", ROWS),

@@ -111,6 +111,8 @@ def test_decision_hand_examples(ex):
     masked = np.array(ex["mask"], bool)
     U = ostep.decide(conf, masked, np.float32(ex["tau"]))
     assert U.astype(int).tolist() == ex["unmask"]
+    U2, fb = ostep.decide(conf, masked, np.float32(ex["tau"]), return_fallback=True)
+    assert np.array_equal(U, U2) and int(fb) == ex["fallback"] and int(U.sum()) == ex["unmasked"]
     new_mask = masked & ~U
     assert new_mask.astype(int).tolist() == ex["new_mask"]
     done = int(not new_mask.any())
@@ -155,6 +157,9 @@ def test_step_hand_example_full():
     assert out["conf"][0, 0] == pytest.approx(math.exp(9) / (math.exp(9) + 3))
     assert out["conf"][1, 3] == pytest.approx(math.exp(3) / (math.exp(3) + 3))
     assert out["conf"][0, 2] == -1.0
+    # row 0 unmasks its two slots above 0.9; row 1 has none above, so its fallback takes one
+    assert out["unmasked"].tolist() == [2, 1]
+    assert out["fallback"].tolist() == [0, 1]
 
 
 def test_step_invariants_random():
