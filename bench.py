@@ -492,12 +492,48 @@ def run_gpu(args):
     }
 
 
-def run_loop(name, mode):
+# masked-position buckets of the per-step scoring table
+M_BUCKETS = (1, 256, 1024, 2048, 4096, 8192, 12288, 16385)
+
+
+def per_step_table(recs, V, es):
+    """recs: (masked positions, rows, scoring-kernel ms, the same logits scored again ms or None) per
+    step -> rows of a table by masked-position bucket: steps, mean us, GB/s of each timing."""
+    import numpy as np
+    out = []
+    M = np.array([r[0] for r in recs], np.float64)
+    ta = np.array([r[2] for r in recs], np.float64) * 1e-3
+    tb = np.array([r[3] if r[3] is not None else np.nan for r in recs], np.float64) * 1e-3
+    for lo, hi in zip(M_BUCKETS[:-1], M_BUCKETS[1:]):
+        sel = (M >= lo) & (M < hi)
+        if not sel.any():
+            continue
+        by = M[sel].sum() * V * es
+        row = {"masked": f"[{lo}, {hi})", "steps": int(sel.sum()), "mean_masked": float(M[sel].mean()),
+               "score_us": float(ta[sel].mean() * 1e6), "score_GBps": float(by / ta[sel].sum() / 1e9)}
+        if not np.isnan(tb[sel]).all():
+            row["rescore_us"] = float(tb[sel].mean() * 1e6)
+            row["rescore_GBps"] = float(by / tb[sel].sum() / 1e9)
+        out.append(row)
+    tot = M.sum() * V * es
+    summary = {"steps": len(recs), "score_GBps": float(tot / ta.sum() / 1e9),
+               "score_frac": float(tot / ta.sum() / 1e9 / PEAK_HBM_GBPS)}
+    if not np.isnan(tb).all():
+        summary["rescore_GBps"] = float(tot / tb.sum() / 1e9)
+        summary["rescore_frac"] = float(tot / tb.sum() / 1e9 / PEAK_HBM_GBPS)
+    return out, summary
+
+
+def run_loop(name, mode, per_step=False, rescore=False):
     """A whole loop of one workload on the GPU (forward = the synthetic generator on the
     device), with its accounting: batch steps, request-steps, idle request-steps (rows stepped
-    after their block finished), scheduler rounds and masked positions scored."""
+    after their block finished), scheduler rounds and masked positions scored.  per_step: every
+    step's scoring kernel timed by kernel-bound events and tabulated by masked-position count
+    (with rescore, the same logits are scored a second time right after, once the forward's
+    writes are long finished, and timed the same way)."""
     import torch
 
+    from confidence_block_unmasking_amd import api
     from confidence_block_unmasking_amd.driver import Session
     from workload import configs, synth
     w = configs.make(name)
@@ -508,12 +544,37 @@ def run_loop(name, mode):
     def fwd(sess):
         synth.logits_gpu(sess.logits, w.dtype, sess.rows, w.L, w.V, sess.row_req, sess.b_rows,
                          sess.masks[sess.cur], w.logit_seed, w.sigma, w.umax)
+    recs = []
+
+    def timed_step(sess, M):
+        # the step as its two halves, the scoring kernel (and its repeat) bound to HIP events
+        nxt = 1 - sess.cur
+        rows, L, V = sess.rows, sess.L, sess.V
+        kw = dict(rows=rows, L=L, V=V, pos_stride=V, row_stride=L * V)
+        ea = api.KernelEvents()
+        api.dllm_step_score_timed(sess.logits, sess.masks[sess.cur], sess.workspace, sess.status, ea, **kw)
+        eb = None
+        if rescore:
+            eb = api.KernelEvents()
+            api.dllm_step_score_timed(sess.logits, sess.masks[sess.cur], sess.workspace, sess.status, eb, **kw)
+        api.dllm_step_decide(sess.dtype, rows, L, V, sess.box(), sess.masks[sess.cur], sess.masks[nxt], sess.tau,
+                             sess.done, sess.accept, sess.workspace, sess.status, p=sess.p_rows, b=sess.b_rows,
+                             conf=sess.conf, argmax=sess.argmax)
+        sess.cur = nxt
+        recs.append((M, rows, ea, eb))
     sess = Session.from_workload(w)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    st = sess.run(mode, fwd, timed=True)
+    st = sess.run(mode, fwd, timed=not per_step, step_fn=timed_step if per_step else None)
     torch.cuda.synchronize()
     sec = time.perf_counter() - t0
+    if per_step:
+        table, summary = per_step_table([(m, r, ea.elapsed_ms(), eb.elapsed_ms() if eb else None)
+                                         for m, r, ea, eb in recs], w.V, w.elem_bytes)
+        return {"loop": w.name, "mode": mode, "steps": st["steps"], "positions_scored": st["positions_scored"],
+                "scoring_by_masked_positions": table, "scoring_overall": summary,
+                "what": "scoring kernel per step by kernel-bound HIP events (dllm_step_score_timed)" +
+                        ("; rescore: the same logits scored again right after the first scoring" if rescore else "")}
     ph = sess.phase_ms()
     ph["host"] = sec * 1e3 - sum(ph.values())
     keys = ("steps", "request_steps", "idle_request_steps", "rounds", "positions_scored", "evicted", "admitted",
@@ -551,6 +612,10 @@ def main():
                     help="instead of the step benchmark, run a whole loop: llada-sync, blockserve-mixed or large-fdfo")
     ap.add_argument("--mode", choices=("sync", "fdfo", "handback"), default=None,
                     help="loop mode for --loop (default: the workload's own)")
+    ap.add_argument("--per-step", action="store_true",
+                    help="with --loop: time every step's scoring kernel and tabulate it by masked positions")
+    ap.add_argument("--rescore", action="store_true",
+                    help="with --per-step: score each step's logits a second time and time that too")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -574,6 +639,9 @@ def main():
         from workload import configs
         if args.loop not in configs.LOOPS:
             raise SystemExit(f"--loop takes one of {', '.join(configs.LOOPS)}")
+        if args.per_step:
+            print(json.dumps(run_loop(args.loop, args.mode, per_step=True, rescore=args.rescore)), flush=True)
+            return
         cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, args.loop)
         out = run_loop(args.loop, args.mode)
         if cpu is not None:

@@ -184,7 +184,8 @@ class Session:
         return self.features_buf[:self.rows * api.N_FEATURES].view(self.rows, api.N_FEATURES)
 
     # ---- the loop rule ----------------------------------------------------------------------------
-    def run(self, mode, forward, max_steps=10**7, on_step=None, timed=False, max_rounds=0, metrics=False):
+    def run(self, mode, forward, max_steps=10**7, on_step=None, timed=False, max_rounds=0, metrics=False,
+            step_fn=None):
         """Drive compact -> pack -> (forward, step)* -> compact ... until queue and rows are empty.
 
         mode: "sync" (the batch runs until every block is done), "fdfo" (first-done-first-out with
@@ -198,7 +199,9 @@ class Session:
         The stats always count the tokens unmasked; metrics=True also reads back the step's per-row
         fallback flags (dllm_step_decide's report: no masked confidence above the threshold) and the
         row map, to count the fallback row-steps and the steps each finished block took
-        (stats["block_steps"]: steps -> blocks).
+        (stats["block_steps"]: steps -> blocks).  step_fn(session, masked_positions), when given,
+        enqueues each step in place of step() (it must leave the new mask in the other mask buffer
+        and switch to it, as step() does); measurement code uses it to time the kernels one by one.
         Returns self.stats."""
         assert mode in ("sync", "fdfo", "handback")
         self.compact(with_box=False, timed=timed)    # admission at the start of the run
@@ -217,7 +220,10 @@ class Session:
                 self.stats["idle_request_steps"] += int((~masked_rows).sum())
                 self.stats["positions_scored"] += int(masked.sum())
                 self._timed("forward", timed, lambda ev: _around(ev, lambda: forward(self)))
-                self.step(timed=timed, report=metrics)
+                if step_fn is not None:
+                    step_fn(self, int(masked.sum()))
+                else:
+                    self.step(timed=timed, report=metrics)
                 done, mask_host, st = self._readback()
                 if st != 0:
                     raise api.DllmError(st, "dllm_step", "(device status)")
