@@ -39,10 +39,11 @@ PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_dream_dynamic_traffic.json")
 # the scoring kernel's sources (with what they include): the traffic figure is reported only while
 # their code, comments and spacing aside, is unchanged
-SCORE_SRC = [os.path.join(ROOT, "confidence_block_unmasking_amd", "csrc", f) for f in ("score.hip", "step_common.h",
-                                                                                      "common.h")] + \
+SCORE_SRC = [os.path.join(ROOT, "confidence_block_unmasking_amd", "csrc", f) for f in ("score.hip", "decide.hip",
+                                                                                      "step_common.h", "common.h")] + \
             [os.path.join(ROOT, "include", "dllm.h")]
 SCORE_KERNEL = "score_kernel"
+DECIDE_KERNEL = "decide_kernel<0, 4>"      # the threshold rule at L <= 32
 COPY_MIB = 256
 SAMPLES = 50          # event-timed steps of each kind after the timed region
 DEFAULT_STEP = "dream-dynamic-step"
@@ -191,22 +192,26 @@ def _per_dispatch(rows, kernel_pred, counter):
 
 
 def record_traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, masked):
-    """Median KiB per dispatch of FETCH_SIZE and WRITE_SIZE for the scoring kernel, each scaled by
-    (known bytes / counted bytes) of a plain copy of COPY_MIB MiB; written to TRAFFIC_FILE."""
-    is_score = lambda n: SCORE_KERNEL in n  # noqa: E731
+    """Median KiB per dispatch of FETCH_SIZE and WRITE_SIZE for the scoring and the deciding kernel,
+    each scaled by (known bytes / counted bytes) of a plain copy of COPY_MIB MiB; written to
+    TRAFFIC_FILE with their sum, the HBM bytes of one dllm_step."""
     is_copy = lambda n: "copyBuffer" in n or "copy" in n.lower()  # noqa: E731
     known_kib = COPY_MIB * 1024.0
-    f_kib, nf = _per_dispatch(_pmc_rows(fetch_dir), is_score, "FETCH_SIZE")
-    w_kib, nw = _per_dispatch(_pmc_rows(write_dir), is_score, "WRITE_SIZE")
     cf_kib, _ = _per_dispatch(_pmc_rows(cfetch_dir), is_copy, "FETCH_SIZE")
     cw_kib, _ = _per_dispatch(_pmc_rows(cwrite_dir), is_copy, "WRITE_SIZE")
     sf, sw = known_kib / cf_kib, known_kib / cw_kib
-    rec = {"kernel": SCORE_KERNEL, "workload": "Dream-shaped dynamic-threshold step (64 x 32 x 152064 bf16)",
-           "masked_positions": masked, "source_sha256": _sha(SCORE_SRC),
-           "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
-           "copy_mib": COPY_MIB, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
-           "fetch_scale": sf, "write_scale": sw,
-           "hbm_bytes_per_launch": (f_kib * sf + w_kib * sw) * 1024.0}
+    fetch, write = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    rec = {"workload": "Dream-shaped dynamic-threshold step (64 x 32 x 152064 bf16)", "masked_positions": masked,
+           "source_sha256": _sha(SCORE_SRC), "copy_mib": COPY_MIB, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
+           "fetch_scale": sf, "write_scale": sw}
+    for key, name in (("score_kernel", SCORE_KERNEL), ("decide_kernel", DECIDE_KERNEL)):
+        pred = (lambda n, name=name: name in n and "score_kernel<false" not in n and "score_kernel<true, false" not in n)
+        f_kib, nf = _per_dispatch(fetch, pred, "FETCH_SIZE")
+        w_kib, nw = _per_dispatch(write, pred, "WRITE_SIZE")
+        rec[key] = {"kernel": name, "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+                    "dispatches": [nf, nw], "hbm_bytes_per_launch": (f_kib * sf + w_kib * sw) * 1024.0}
+    rec["hbm_bytes_per_launch"] = rec["score_kernel"]["hbm_bytes_per_launch"]
+    rec["dllm_step_hbm_bytes"] = rec["score_kernel"]["hbm_bytes_per_launch"] + rec["decide_kernel"]["hbm_bytes_per_launch"]
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -214,13 +219,15 @@ def record_traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, masked):
 
 
 def stored_traffic(masked):
+    """(scoring kernel, whole dllm_step) HBM bytes per launch from TRAFFIC_FILE, or (None, None) when
+    the kernels' code changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None
+        return None, None
     with open(TRAFFIC_FILE) as f:
         tr = json.load(f)
     if tr.get("source_sha256") != _sha(SCORE_SRC) or tr.get("masked_positions") != masked:
-        return None                       # the kernel changed since the counters were taken
-    return tr.get("hbm_bytes_per_launch")
+        return None, None
+    return tr.get("hbm_bytes_per_launch"), tr.get("dllm_step_hbm_bytes")
 
 
 # ---- the timed device path ---------------------------------------------------------------------
@@ -439,8 +446,8 @@ def run_gpu(args):
         return {"samples": int(us.size), "mean": float(us.mean()), "p10": float(np.percentile(us, 10)),
                 "p50": float(np.percentile(us, 50)), "p90": float(np.percentile(us, 90))}
     kern_achieved = timed_bytes / (float(kern_ms.mean()) * 1e-3) / 1e9
-    traffic = (stored_traffic(M) if args.shards <= 1 and args.rule == "threshold" and args.step == DEFAULT_STEP
-               else None)
+    traffic, step_traffic = (stored_traffic(M) if args.shards <= 1 and args.rule == "threshold"
+                             and args.step == DEFAULT_STEP else (None, None))
     score_roof = {"kernel": "score_kernel", "achieved": kern_achieved, "frac": kern_achieved / PEAK_HBM_GBPS,
                   "samples": int(kern_ms.size), "traffic": traffic}
     if step_ms.size:
@@ -449,7 +456,7 @@ def run_gpu(args):
         achieved = step_bytes / (float(step_ms.mean()) * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": "dllm_step (score_kernel start to decide_kernel end)",
                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                    "traffic": traffic, "samples": int(step_ms.size), "score_kernel": score_roof}
+                    "traffic": step_traffic, "samples": int(step_ms.size), "score_kernel": score_roof}
     else:
         roofline = {"bound": "hbm", "kernel": "score_kernel", "achieved": kern_achieved, "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": kern_achieved / PEAK_HBM_GBPS, "traffic": traffic,

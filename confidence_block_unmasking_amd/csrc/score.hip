@@ -28,7 +28,8 @@ namespace dllm {
 
 // Kernel 1: score every chunk of every masked slot.
 template <bool BF16, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void score_kernel(StepParams P, int win) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(StepParams P,
+                                                                                                 int win) {
     extern __shared__ int s_id[];              // [win] slot index (row*L + j) of the window's masked slots
     __shared__ int s_tmp[2][kWaves];
     __shared__ int s_next;
@@ -174,10 +175,13 @@ dllm_status launch_score(const StepParams &P, int32_t dtype, hipStream_t st, hip
     // vector path: 16-byte aligned rows whose length is a whole number of 16-byte vectors
     const bool aligned = ((uintptr_t)P.logits & 15) == 0 && (P.pos_stride_b & 15) == 0 &&
                          (P.row_stride_b & 15) == 0 && (P.V % (16 / es)) == 0;
-    // grid: one workgroup per compute unit; more when the LDS window of masked slots would
-    // exceed 2048 entries (8 KiB of dynamic LDS); fewer when a fully masked box has fewer chunks
-    // than that many waves
-    int64_t grid = cu_count();
+    // grid: kGroupsPerCU workgroups per compute unit, each with an even static share; two are
+    // resident on a unit at a time, and as one finishes the dispatcher starts the next on that
+    // unit, which evens out the units of an XCD at the end (and overlaps each workgroup's
+    // prologue with its neighbour's streaming).  More workgroups when the LDS window of masked
+    // slots would exceed 2048 entries (8 KiB of dynamic LDS); fewer when a fully masked box has
+    // fewer chunks than that many waves.
+    int64_t grid = (int64_t)cu_count() * kGroupsPerCU;
     if (grid < (S + 2047) / 2048) grid = (S + 2047) / 2048;
     const int64_t most = (S * NC + kWaves - 1) / kWaves;
     if (grid > most) grid = most;

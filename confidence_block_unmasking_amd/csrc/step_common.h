@@ -20,7 +20,14 @@ namespace dllm {
 #define DLLM_STEP_ACC 4               // running sums per lane in the chunk reduction (a power of two)
 #endif
 
-constexpr int kWaves = DLLM_STEP_WAVES;       // waves per scoring workgroup (one workgroup per CU)
+#ifndef DLLM_STEP_GROUPS_PER_CU
+#define DLLM_STEP_GROUPS_PER_CU 4
+#endif
+
+constexpr int kWaves = DLLM_STEP_WAVES;       // waves per scoring workgroup
+// Scoring workgroups per compute unit over the launch.  Two fit a unit at a time (the kernel keeps
+// to 128 VGPRs: four waves per SIMD); the hardware dispatcher hands the rest out as units free up.
+constexpr int kGroupsPerCU = DLLM_STEP_GROUPS_PER_CU;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kVPL = DLLM_STEP_VPL;           // 16-byte vectors per lane per chunk
 constexpr int kCH = 64 * kVPL;                // vectors per chunk

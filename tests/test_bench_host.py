@@ -50,26 +50,32 @@ def test_record_and_report_traffic(bench, tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "SCORE_SRC", [src])
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
     kern = "void dllm::score_kernel<true, true>(dllm::StepParams, int)"
+    dec = "void dllm::decide_kernel<0, 4>(dllm::StepParams)"
     # two counter instances per dispatch (summed), three dispatches (median taken)
     fetch = _pmc_csv(tmp_path / "f", [(1, kern, "FETCH_SIZE", 40.0), (1, kern, "FETCH_SIZE", 60.0),
                                       (2, kern, "FETCH_SIZE", 100.0), (3, kern, "FETCH_SIZE", 500.0),
-                                      (4, "other", "FETCH_SIZE", 9e9)])
+                                      (4, "other", "FETCH_SIZE", 9e9), (5, dec, "FETCH_SIZE", 6.0),
+                                      (6, dec, "FETCH_SIZE", 8.0), (7, dec, "FETCH_SIZE", 7.0)])
     write = _pmc_csv(tmp_path / "w", [(1, kern, "WRITE_SIZE", 3.0), (2, kern, "WRITE_SIZE", 5.0),
-                                      (3, kern, "WRITE_SIZE", 4.0)])
+                                      (3, kern, "WRITE_SIZE", 4.0), (5, dec, "WRITE_SIZE", 2.0)])
     known = bench.COPY_MIB * 1024.0
     cfetch = _pmc_csv(tmp_path / "cf", [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", known / 2)])
     cwrite = _pmc_csv(tmp_path / "cw", [(1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", known)])
     bench.record_traffic(fetch, write, cfetch, cwrite, masked=7)
     rec = json.load(open(bench.TRAFFIC_FILE))
-    assert rec["fetch_kib_per_dispatch"] == 100.0 and rec["write_kib_per_dispatch"] == 4.0
+    sk = rec["score_kernel"]
+    assert sk["fetch_kib_per_dispatch"] == 100.0 and sk["write_kib_per_dispatch"] == 4.0
     assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
-    assert rec["hbm_bytes_per_launch"] == pytest.approx((100.0 * 2 + 4.0) * 1024)
-    assert bench.stored_traffic(7) == pytest.approx((100.0 * 2 + 4.0) * 1024)
-    assert bench.stored_traffic(8) is None                       # another workload
+    score = (100.0 * 2 + 4.0) * 1024
+    step = score + (7.0 * 2 + 2.0) * 1024
+    assert rec["hbm_bytes_per_launch"] == pytest.approx(score)
+    assert rec["dllm_step_hbm_bytes"] == pytest.approx(step)
+    assert bench.stored_traffic(7) == pytest.approx((score, step))
+    assert bench.stored_traffic(8) == (None, None)               # another workload
     _write(src, "void k() { int x; }")
-    assert bench.stored_traffic(7) is None                       # the kernel's code changed
+    assert bench.stored_traffic(7) == (None, None)               # the kernels' code changed
     _write(src, "void k() {} // a comment only")
-    assert bench.stored_traffic(7) is not None
+    assert bench.stored_traffic(7) != (None, None)
 
 
 def test_more_than_one_gpu_is_refused():
