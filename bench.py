@@ -569,6 +569,12 @@ def run_loop(name, mode, per_step=False, rescore=False):
                              conf=sess.conf, argmax=sess.argmax)
         sess.cur = nxt
         recs.append((M, rows, ea, eb))
+    # one scheduler round of a throwaway session first, so that every kernel's first launch (code
+    # object loading) is outside the timed loop
+    warm = Session.from_workload(w)
+    warm.run(mode, fwd, max_rounds=1)
+    torch.cuda.synchronize()
+    del warm
     sess = Session.from_workload(w)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
