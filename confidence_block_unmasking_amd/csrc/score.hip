@@ -178,10 +178,17 @@ dllm_status launch_score(const StepParams &P, int32_t dtype, hipStream_t st, hip
     // grid: kGroupsPerCU workgroups per compute unit, each with an even static share; two are
     // resident on a unit at a time, and as one finishes the dispatcher starts the next on that
     // unit, which evens out the units of an XCD at the end (and overlaps each workgroup's
-    // prologue with its neighbour's streaming).  More workgroups when the LDS window of masked
-    // slots would exceed 2048 entries (8 KiB of dynamic LDS); fewer when a fully masked box has
-    // fewer chunks than that many waves.
-    int64_t grid = (int64_t)cu_count() * kGroupsPerCU;
+    // prologue with its neighbour's streaming).  Small boxes, whose chunks could not reach
+    // kSmallBoxChunksPerCU per unit even if every slot were masked, take two workgroups per unit
+    // (both resident at once), and the smallest (kTinyBoxChunksPerCU) one: there a workgroup would
+    // otherwise get only a few chunks, and each extra workgroup is one more prologue.  More
+    // workgroups when the LDS window of masked slots would exceed 2048 entries (8 KiB of dynamic
+    // LDS); fewer when a fully masked box has fewer chunks than that many waves.
+    const int64_t cus = cu_count();
+    const int64_t box_chunks = S * NC;
+    int64_t grid = cus * (box_chunks < cus * kTinyBoxChunksPerCU    ? 1
+                          : box_chunks < cus * kSmallBoxChunksPerCU ? 2
+                                                                   : kGroupsPerCU);
     if (grid < (S + 2047) / 2048) grid = (S + 2047) / 2048;
     const int64_t most = (S * NC + kWaves - 1) / kWaves;
     if (grid > most) grid = most;

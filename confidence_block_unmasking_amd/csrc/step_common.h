@@ -28,6 +28,10 @@ constexpr int kWaves = DLLM_STEP_WAVES;       // waves per scoring workgroup
 // Scoring workgroups per compute unit over the launch.  Two fit a unit at a time (the kernel keeps
 // to 128 VGPRs: four waves per SIMD); the hardware dispatcher hands the rest out as units free up.
 constexpr int kGroupsPerCU = DLLM_STEP_GROUPS_PER_CU;
+// Box sizes (rows * L * chunks per slot, per compute unit) below which the scoring grid is two
+// workgroups per unit, and one.
+constexpr int kSmallBoxChunksPerCU = 140;
+constexpr int kTinyBoxChunksPerCU = 24;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kVPL = DLLM_STEP_VPL;           // 16-byte vectors per lane per chunk
 constexpr int kCH = 64 * kVPL;                // vectors per chunk
