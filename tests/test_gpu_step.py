@@ -219,6 +219,23 @@ def test_step_many_slots(rows, L, V, dtype, p_mask, moff):
     check_step(logits, dtype, ids, mask, tau, g)
 
 
+@pytest.mark.parametrize("per_cu", [24, 140])
+@pytest.mark.parametrize("delta", [-32, 0, 32])
+def test_step_at_the_grid_thresholds(per_cu, delta):
+    # boxes of just under, at and just over 24 and 140 chunks per compute unit (one chunk per slot
+    # here), where the scoring grid changes from one to two to four workgroups per unit
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    S = per_cu * cu + delta
+    L = 32
+    rows = S // L
+    rng = np.random.default_rng(per_cu * 100 + delta)
+    logits, ids, mask, tau = _rand_case(rng, rows, L, 64, "bf16", p_mask=0.5)
+    print(f"grid threshold {per_cu}/CU x {cu} CUs {delta:+d}: rows={rows} L={L}", flush=True)
+    g = gpu_step(logits, "bf16", ids, mask, tau)
+    assert g["status"] == 0
+    check_step(logits, "bf16", ids, mask, tau, g)
+
+
 def test_step_at_the_position_limit():
     # rows * L = DLLM_MAX_POSITIONS slots in one call (rows = DLLM_MAX_ROWS)
     from confidence_block_unmasking_amd import _lib
