@@ -9,7 +9,8 @@
 // How (gfx950).  A streaming reduction over M masked slots x V logits, bound by HBM.  Each row is
 // cut into NC chunks of 64*kVPL 16-byte vectors (the last one shorter); the cut depends on V only,
 // so a slot's result never depends on the rest of the batch.  The M*NC chunks are split evenly
-// over the workgroups, one workgroup per compute unit holding all of that unit's waves.  Inside a
+// over the workgroups: four per compute unit, two resident at a time, so that as one finishes the
+// dispatcher starts the next on that unit (fewer for small boxes; see launch_score).  Inside a
 // workgroup the waves take chunks one at a time from an LDS counter: the sequencer favours older
 // waves when they compete for the memory pipe, so a fixed split per wave leaves the young ones
 // finishing last, while a shared counter lets every wave of the unit finish within about one chunk

@@ -12,7 +12,7 @@
 //   1. score_kernel streams every masked slot's vocabulary row once.  Each row is cut into NC
 //      chunks of 64*kVPL 16-byte vectors (the last one shorter); the cut depends on V only, so a
 //      slot's result never depends on the rest of the batch.  The M*NC chunks are split evenly
-//      over the workgroups, one workgroup per compute unit holding all of that unit's waves.
+//      over the workgroups (four per compute unit, two resident at a time; fewer for small boxes).
 //      Inside a workgroup the waves take chunks one at a time from an LDS counter: the sequencer
 //      favours older waves when they compete for the memory pipe, so a fixed split per wave
 //      leaves the young ones finishing last, while a shared counter lets every wave of the unit
@@ -20,7 +20,8 @@
 //      units but cost a memory round trip each and serialise on one address.)
 //      One wavefront reduces one chunk: 64 lanes issue kVPL coalesced 16-byte non-temporal loads
 //      each (1 KiB per wave instruction), the next chunk's loads go out before this chunk's
-//      arithmetic, each element costs one FMA and one v_exp (sum of exp2(x*log2e - max*log2e)),
+//      arithmetic, each element costs an unpack, a share of a max3, one FMA, one v_exp and one add
+//      (sum of exp2(x*log2e - max*log2e)),
 //      and lanes combine through DPP.  The chunk partial (max, sum, first element index at the
 //      max) stays in a lane register until the wave has 64 of them or runs out of chunks, then
 //      they leave in one store: a store between the loads of consecutive chunks would hold back
@@ -28,10 +29,10 @@
 //   2. decide_kernel, one workgroup per row, merges each masked slot's NC partials in chunk order
 //      (a fixed tree, so the bits are reproducible), and applies the unmask rule to the row.
 //   The launch boundary is what makes the partials of kernel 1 visible to kernel 2.  A one-launch
-//   variant (the last workgroup to finish a row decides it) needs a device-wide release and
-//   acquire per workgroup; with device-coherent stores and loads standing in for those fences it
-//   read stale partials on this part, and its in-kernel decision was no faster than the second
-//   launch.  No MFMA: there is no contraction here.
+//   variant (the last workgroup to finish a row decides it) needs an agent-scope release (an L2
+//   write-back) in every scoring workgroup and an acquire in the deciding one; the release alone
+//   costs more than the whole second launch on this part.  With device-coherent stores and loads
+//   standing in for those fences it read stale partials.  No MFMA: there is no contraction here.
 //
 // This file holds the argument checks and the C entry points; the kernels are in score.hip and
 // decide.hip, their shared definitions in step_common.h.
