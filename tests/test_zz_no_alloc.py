@@ -80,3 +80,24 @@ def test_noalloc_step_equals_dllm_step_on_two_calls_in_a_row():
             assert np.array_equal(got["arg"][r:r + 1], o["argmax"])
             assert np.abs(got["conf"][r:r + 1].astype(np.float64) - o["conf"]).max() <= 1e-5
             assert np.array_equal(got["ids"][r:r + 1], o["ids"]) and np.array_equal(got["mask_out"][r:r + 1], o["mask"])
+
+
+def test_noalloc_step_at_the_scratch_capacity():
+    """The largest box the scratch array holds at V = 152064 bf16 (3942 x 7 = 27 594 slots of 38
+    chunks: 16 777 056 bytes of partials, 160 short of 16 MiB), then the Dream-shaped box again:
+    equal to dllm_step."""
+    from confidence_block_unmasking_amd import _lib, api
+    rows, L, V = 3942, 7, 152064
+    assert api.dllm_step_workspace_bytes(rows, L, V) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert api.dllm_step_workspace_bytes(rows + 1, L, V) > _lib.NOALLOC_SCRATCH_BYTES
+    for rows, L, W in ((3942, 7, 40), (64, 32, 600)):
+        print(f"noalloc capacity: rows={rows} L={L} V={V} bf16", flush=True)
+        c = _case(rows, L, V, "bf16", 7 + rows, W)
+        ref = _run(c, noalloc=False)
+        got = _run(c, noalloc=True)
+        assert int(got["status"][0]) == 0 and int(ref["status"][0]) == 0
+        for k in ("ids", "mask_out", "done", "acc", "arg"):
+            assert np.array_equal(got[k], ref[k]), k
+        assert np.array_equal(got["conf"].view(np.uint32), ref["conf"].view(np.uint32)), "conf bits"
+        del c
+        torch.cuda.empty_cache()
